@@ -1,0 +1,25 @@
+"""Reference oracle for the attention forward: plain, slow, fp64, CPU only.
+
+This package is test infrastructure. Only the tests, the smoke check and the
+benchmark's CPU-baseline leg import it; the GPU library never does, and it shares
+no code, tables or helpers with the HIP path.
+
+Sources (the three pages on IO-aware softmax attention):
+  * "Flash Attention (FA1)" (languisher.top), section "Naive Attention 问题分析":
+    safe softmax definition m(x) = max_i x_i, softmax = e^{x-m} / sum e^{x-m}.
+  * "01 · 注意力为什么是 IO 瓶颈" (ai-reference-codex), section 3 table and
+    section 5 pseudocode: the three textbook steps S = QK^T, P = softmax(S), O = PV.
+  * "Flash Attention (FA1)", section "核心局部状态计算和更新公式推导", steps 1-5:
+    the per-tile update of (m_i, l_i, O_i).
+  * The same page's tiling section: T_r = ceil(N/B_r), T_c = ceil(N/B_c).
+
+Every function is pinned by tests that do not re-type its formulas (closed forms,
+invariants, brute force, library special cases); no function here is "parity
+unpinned".
+"""
+from .attention import (  # noqa: F401
+    attention_fp64,
+    attention_online_fp64,
+    attention_brute_force,
+    attention_unfused_bf16,
+)
