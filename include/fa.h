@@ -1,0 +1,115 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) attention-forward library, libfa.so.
+ *
+ * The library computes the exact attention forward of the FlashAttention pages:
+ *     O   = softmax(scale * Q K^T) V          (row-wise softmax over the keys)
+ *     LSE = per query row, ln sum_j exp(scale * q_i . k_j)
+ * in one fused kernel that never stores the N x N scores or probabilities
+ * ("Flash Attention (FA1)", sections "Tiling in FlashAttention" and
+ * "Online Softmax in FlashAttention"; "01 · 注意力为什么是 IO 瓶颈", section 4:
+ * read Q, K, V once, write O and LSE once). It also ships the textbook
+ * three-kernel computation (same page, section 3 table: S = QK^T to memory,
+ * P = softmax(S) to memory, O = PV) as a traffic baseline, and the block-size
+ * selector ("01 ·" page, section 7: tile sizes are chosen against on-chip
+ * memory capacity).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense, contiguous, row-major [B, H, N, d] (Q, K, V, O; bf16)
+ *     and [B, H, N] (LSE; fp32), in device memory the caller allocated and owns.
+ *     The library allocates nothing on the fused path and keeps no pointer after
+ *     a call returns.
+ *   - d (head dimension) must be 64 or 128. B, H, N >= 0; when B*H*N == 0 the
+ *     call is a no-op that returns FA_OK without touching any pointer.
+ *   - scale must be finite and >= 0 (the pages' scale is 1/sqrt(d) > 0; 0 gives
+ *     the uniform average).
+ *   - Q, K, V, O must be 16-byte aligned; LSE 4-byte aligned. Q, K and V may
+ *     share memory; O and LSE must not overlap any input or each other.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *     are asynchronous: they return after enqueueing the work; faults during
+ *     execution surface at the caller's next synchronisation on that stream.
+ *   - Argument errors are detected before any HIP call and return a negative
+ *     fa_status; nothing is enqueued then. A launch error returns FA_ERR_HIP.
+ *   - The fused result is bitwise deterministic for a given device and shape
+ *     (no atomics, fixed reduction order).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,     /* B, H or N negative */
+  FA_ERR_HEADDIM = -3,   /* d not in {64, 128} */
+  FA_ERR_ALIGN = -4,     /* a pointer is not aligned as stated above */
+  FA_ERR_SCALE = -5,     /* scale not finite or negative */
+  FA_ERR_ALIAS = -6,     /* O or LSE overlaps an input or each other */
+  FA_ERR_OVERFLOW = -7,  /* sizes overflow 64-bit byte counts or the launch grid */
+  FA_ERR_WORKSPACE = -8, /* unfused workspace missing or too small */
+  FA_ERR_HIP = -9,       /* the HIP runtime reported an error */
+  FA_ERR_DEVICE = -10    /* the current device is not gfx950 */
+} fa_status;
+
+/*
+ * Fused attention forward. q, k, v, o: bf16 [B,H,N,d]; lse: fp32 [B,H,N].
+ * Per row i of each (b, h): o[i] = sum_j p_ij v[j] / sum_j p_ij with
+ * p_ij = exp(s_ij - max_j s_ij), s_ij = scale * q[i].k[j]; lse[i] = ln sum_j exp(s_ij).
+ * One kernel launch: Q is tiled by rows, K/V stream through on-chip memory in
+ * column tiles, and the online softmax (running max, running sum, rescaled
+ * accumulator; "Flash Attention (FA1)", derivation steps 1-5) keeps S and P on
+ * chip. O is rounded to bf16 (nearest-even) once, at the end.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, void* stream);
+
+/*
+ * The textbook three-step forward ("01 · 注意力为什么是 IO 瓶颈", section 3
+ * table and section 5): kernel 1 writes S = scale*QK^T (fp32, [B,H,N,Ns]) to the
+ * workspace, kernel 2 reads S and writes P = softmax(S) (bf16, [B,H,N,Ns]) and
+ * LSE, kernel 3 reads P and V and writes O. Same argument rules as fa_fwd, plus
+ * a caller-owned device workspace of at least fa_unfused_workspace_bytes(B,H,N)
+ * bytes, 16-byte aligned, not overlapping any tensor argument.
+ */
+int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_unfused_fwd needs: 6*B*H*N*Ns with Ns = N rounded up to a
+ * multiple of 64 (fp32 S + bf16 P, rows padded), rounded up to 256; 0 if the
+ * product overflows size_t. */
+size_t fa_unfused_workspace_bytes(int B, int H, int N);
+
+/*
+ * Block-size selector: the (query rows per workgroup, keys per tile, waves per
+ * workgroup) the fused kernel uses for this shape ("01 ·" page, section 7: tiles
+ * are sized against on-chip memory). Writes *br, *bc, *nwaves; returns FA_OK,
+ * FA_ERR_NULL or FA_ERR_HEADDIM.
+ */
+int fa_select_blocks(int d, int N, int B, int H, int* br, int* bc, int* nwaves);
+
+/*
+ * Argument validation shared by fa_fwd and fa_unfused_fwd, exposed so callers
+ * can check arguments without a GPU. workspace may be NULL for the fused path
+ * (need_workspace = 0). Pure host code: makes no HIP call.
+ */
+int fa_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                  int B, int H, int N, int d, float scale,
+                  int need_workspace, const void* workspace, size_t workspace_bytes);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

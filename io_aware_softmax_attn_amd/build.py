@@ -1,0 +1,58 @@
+"""Compile the HIP sources of this package into ``libfa.so`` (gfx950 only).
+
+Run ``python -m io_aware_softmax_attn_amd.build`` or call :func:`build_library`.
+The library is written next to this file, in-tree, through a temporary name and
+an atomic rename, so a half-written file is never loaded.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+SOURCES = ["fa_fwd.hip", "fa_unfused.hip", "fa_api.cpp", "fa_select.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libfa.so")
+    return path
+
+
+def compile_command(out: str) -> list[str]:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # packed fp32 VALU ops are kept out of generated code on this part
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        *srcs, "-o", out,
+    ]
+
+
+def build_library(verbose: bool = False) -> str:
+    fd, tmp = tempfile.mkstemp(prefix="libfa.", suffix=".so.tmp", dir=PKG_DIR)
+    os.close(fd)
+    try:
+        cmd = compile_command(tmp)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if verbose or res.returncode != 0:
+            sys.stderr.write(res.stderr)
+        if res.returncode != 0:
+            raise RuntimeError(f"building libfa.so failed (exit {res.returncode}): {' '.join(cmd)}")
+        os.replace(tmp, LIB_PATH)
+    finally:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

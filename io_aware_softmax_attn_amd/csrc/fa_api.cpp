@@ -1,0 +1,130 @@
+// C ABI of libfa.so: argument validation, dispatch and status strings.
+// Plain host C++ (no HIP headers); the HIP work happens behind fa_internal.h.
+#include "../../include/fa.h"
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
+  if (a != 0 && b > std::numeric_limits<uint64_t>::max() / a) return false;
+  *out = a * b;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H and N must be >= 0";
+    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_ALIGN: return "q, k, v, o and workspace must be 16-byte aligned, lse 4-byte aligned";
+    case FA_ERR_SCALE: return "scale must be finite and >= 0";
+    case FA_ERR_ALIAS: return "o or lse overlaps an input, or each other";
+    case FA_ERR_OVERFLOW: return "problem size overflows 64-bit byte counts or the launch grid";
+    case FA_ERR_WORKSPACE: return "unfused workspace is missing, too small, misaligned or overlaps a tensor";
+    case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+    default: return "unknown status";
+  }
+}
+
+size_t fa_unfused_workspace_bytes(int B, int H, int N) {
+  if (B < 0 || H < 0 || N < 0) return 0;
+  // S (fp32) and P (bf16) rows are padded to a multiple of 64 columns.
+  const uint64_t ns = ((uint64_t)N + 63) / 64 * 64;
+  uint64_t rows, sq, bytes;
+  if (!mul_ok((uint64_t)B * (uint64_t)H, (uint64_t)N, &rows)) return 0;
+  if (!mul_ok(rows, ns, &sq)) return 0;
+  if (!mul_ok(sq, 6, &bytes)) return 0;
+  if (bytes > std::numeric_limits<uint64_t>::max() - 255) return 0;
+  bytes = (bytes + 255) & ~uint64_t(255);
+  if (bytes > std::numeric_limits<size_t>::max()) return 0;
+  return (size_t)bytes;
+}
+
+int fa_select_blocks(int d, int N, int B, int H, int* br, int* bc, int* nwaves) {
+  if (!br || !bc || !nwaves) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  const fa::Blocks b = fa::select_blocks(d, N, B, H);
+  *br = b.br;
+  *bc = b.bc;
+  *nwaves = b.nwaves;
+  return FA_OK;
+}
+
+int fa_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                  int B, int H, int N, int d, float scale,
+                  int need_workspace, const void* workspace, size_t workspace_bytes) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!std::isfinite(scale) || scale < 0.0f) return FA_ERR_SCALE;
+  // B, H, N < 2^31, so B*H < 2^62 and B*H*N cannot wrap once B*H < 2^33.
+  if ((uint64_t)B * (uint64_t)H > (std::numeric_limits<uint64_t>::max() >> 31)) return FA_ERR_OVERFLOW;
+  const uint64_t rows64 = (uint64_t)B * (uint64_t)H * (uint64_t)N;
+  if (rows64 == 0) return FA_OK;  // empty problem: nothing is touched
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  uint64_t elems, tbytes, lbytes;
+  if (!mul_ok(rows64, (uint64_t)d, &elems) || !mul_ok(elems, 2, &tbytes) || !mul_ok(rows64, 4, &lbytes))
+    return FA_ERR_OVERFLOW;
+  // Launch grid: one workgroup per (b, h, query tile of the widest block, 256 rows).
+  const uint64_t tiles = ((uint64_t)N + 255) / 256;
+  if ((uint64_t)B * (uint64_t)H * tiles > (uint64_t)std::numeric_limits<int32_t>::max()) return FA_ERR_OVERFLOW;
+  auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
+    return FA_ERR_ALIGN;
+  const size_t tb = (size_t)tbytes, lb = (size_t)lbytes;
+  if (overlaps(o, tb, q, tb) || overlaps(o, tb, k, tb) || overlaps(o, tb, v, tb) || overlaps(lse, lb, q, tb) ||
+      overlaps(lse, lb, k, tb) || overlaps(lse, lb, v, tb) || overlaps(lse, lb, o, tb))
+    return FA_ERR_ALIAS;
+  if (need_workspace) {
+    const size_t need = fa_unfused_workspace_bytes(B, H, N);
+    if (need == 0) return FA_ERR_OVERFLOW;
+    if (!workspace || workspace_bytes < need || misaligned(workspace, 16)) return FA_ERR_WORKSPACE;
+    if (overlaps(workspace, need, q, tb) || overlaps(workspace, need, k, tb) || overlaps(workspace, need, v, tb) ||
+        overlaps(workspace, need, o, tb) || overlaps(workspace, need, lse, lb))
+      return FA_ERR_WORKSPACE;
+  }
+  return FA_OK;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, float scale,
+           void* stream) {
+  const int st = fa_check_args(q, k, v, o, lse, B, H, N, d, scale, 0, nullptr, 0);
+  if (st != FA_OK) return st;
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)N == 0) return FA_OK;
+  const int dev = fa::device_is_gfx950();
+  if (dev < 0) return dev;
+  if (dev == 0) return FA_ERR_DEVICE;
+  return fa::launch_fused(q, k, v, o, lse, B, H, N, d, scale, fa::select_blocks(d, N, B, H), stream);
+}
+
+int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = fa_check_args(q, k, v, o, lse, B, H, N, d, scale, 1, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)N == 0) return FA_OK;
+  const int dev = fa::device_is_gfx950();
+  if (dev < 0) return dev;
+  if (dev == 0) return FA_ERR_DEVICE;
+  return fa::launch_unfused(q, k, v, o, lse, B, H, N, d, scale, workspace, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Internal interface between the host API (fa_api.cpp, plain C++) and the HIP
+// translation units that own the kernels. No HIP types appear here so that the
+// API layer builds with any host compiler.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+namespace fa {
+
+// Tile shape chosen for a problem; filled in by select_blocks.
+struct Blocks {
+  int br;      // query rows per workgroup
+  int bc;      // keys per K/V tile
+  int nwaves;  // 64-lane waves per workgroup
+};
+
+// Picks the fused kernel's tile shape (see fa_select.cpp).
+Blocks select_blocks(int d, int N, int B, int H);
+
+// Enqueue the fused forward; returns a fa_status code. Arguments already validated.
+int launch_fused(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, const Blocks& blk, void* stream);
+
+// Enqueue the three unfused kernels; returns a fa_status code.
+int launch_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, void* workspace, void* stream);
+
+// 1 if the current device is gfx950, 0 if not, negative fa_status on HIP error.
+int device_is_gfx950();
+
+}  // namespace fa

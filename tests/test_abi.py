@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/fa.h, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import io_aware_softmax_attn_amd as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks", "fa_check_args",
+              "fa_status_string", "fa_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(fa):
+    dll = ctypes.CDLL(fa.build.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(dll, n), f"libfa.so does not export {n}"
+
+
+def test_exported_symbols_are_c_linkage(fa):
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    out = subprocess.run([nm, "-D", "--defined-only", fa.build.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(fa_[a-z_0-9]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings(fa):
+    assert fa.fa_version() >= 10000
+    for name, code in fa.STATUS.items():
+        s = fa.fa_status_string(code)
+        assert s and s != "unknown status", name
+    assert fa.fa_status_string(12345) == "unknown status"
+
+
+def test_select_blocks(fa):
+    for d in (64, 128):
+        br, bc, nw = fa.fa_select_blocks(d, 8192)
+        assert br == 64 * nw and bc in (32, 64, 128) and nw >= 1
+        # LDS budget: three K/V stages fit the 160 KB of a CU
+        assert 3 * 2 * bc * d * 2 <= 160 * 1024
+    with pytest.raises(ValueError):
+        fa.fa_select_blocks(96, 128)
+
+
+def test_workspace_bytes(fa):
+    for B, H, N in ((1, 1, 256), (4, 16, 1024), (1, 8, 30001), (2, 3, 1)):
+        ns = (N + 63) // 64 * 64
+        want = (6 * B * H * N * ns + 255) // 256 * 256
+        assert fa.fa_unfused_workspace_bytes(B, H, N) == want
+    assert fa.fa_unfused_workspace_bytes(-1, 1, 1) == 0
+    assert fa.fa_unfused_workspace_bytes(2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1) == 0
+
+
+A = 1 << 20  # fake, well-separated, aligned addresses: validation never dereferences
+
+
+def ptrs(n=1 << 12):
+    return [A, 2 * A, 3 * A, 4 * A, 5 * A]
+
+
+def check(fa, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=2, N=64, d=128, scale=0.1, ws=0, wsp=None, wsb=0):
+    return fa.fa_check_args(q, k, v, o, lse, B, H, N, d, scale, ws, wsp, wsb)
+
+
+def test_check_args_ok(fa):
+    assert check(fa) == 0
+    assert check(fa, q=A, k=A, v=A) == 0  # inputs may share memory
+    assert check(fa, scale=0.0) == 0
+
+
+def test_check_args_errors(fa):
+    S = fa.STATUS
+    assert check(fa, B=-1) == S["FA_ERR_SHAPE"]
+    assert check(fa, N=-5) == S["FA_ERR_SHAPE"]
+    assert check(fa, d=96) == S["FA_ERR_HEADDIM"]
+    assert check(fa, d=256) == S["FA_ERR_HEADDIM"]
+    assert check(fa, scale=float("nan")) == S["FA_ERR_SCALE"]
+    assert check(fa, scale=float("inf")) == S["FA_ERR_SCALE"]
+    assert check(fa, scale=-0.5) == S["FA_ERR_SCALE"]
+    assert check(fa, q=None) == S["FA_ERR_NULL"]
+    assert check(fa, lse=None) == S["FA_ERR_NULL"]
+    assert check(fa, q=A + 8) == S["FA_ERR_ALIGN"]
+    assert check(fa, o=4 * A + 4) == S["FA_ERR_ALIGN"]
+    assert check(fa, lse=5 * A + 2) == S["FA_ERR_ALIGN"]
+    assert check(fa, o=A) == S["FA_ERR_ALIAS"]
+    assert check(fa, o=A + 16) == S["FA_ERR_ALIAS"]  # partial overlap with q
+    assert check(fa, lse=4 * A + 64) == S["FA_ERR_ALIAS"]  # inside o
+    assert check(fa, B=1 << 30, H=1 << 30, N=1 << 30) == S["FA_ERR_OVERFLOW"]
+    assert check(fa, B=1 << 16, H=1 << 16, N=1 << 20) == S["FA_ERR_OVERFLOW"]  # grid too large
+
+
+def test_check_args_empty_problem_ignores_pointers(fa):
+    assert check(fa, q=None, k=None, v=None, o=None, lse=None, N=0) == 0
+    assert check(fa, q=None, k=None, v=None, o=None, lse=None, B=0) == 0
+
+
+def test_check_args_workspace(fa):
+    S = fa.STATUS
+    need = fa.fa_unfused_workspace_bytes(1, 2, 64)
+    W = 16 * A
+    assert check(fa, ws=1, wsp=W, wsb=need) == 0
+    assert check(fa, ws=1, wsp=None, wsb=need) == S["FA_ERR_WORKSPACE"]
+    assert check(fa, ws=1, wsp=W, wsb=need - 1) == S["FA_ERR_WORKSPACE"]
+    assert check(fa, ws=1, wsp=W + 4, wsb=need) == S["FA_ERR_WORKSPACE"]
+    assert check(fa, ws=1, wsp=A, wsb=need) == S["FA_ERR_WORKSPACE"]  # overlaps q
+
+
+def test_fwd_rejects_before_any_hip_call(fa):
+    """Argument errors return their code without touching the device (no GPU here)."""
+    S = fa.STATUS
+    lib = fa.lib
+    assert lib.fa_fwd(None, None, None, None, None, 1, 1, 64, 96, 0.1, None) == S["FA_ERR_HEADDIM"]
+    assert lib.fa_fwd(A, 2 * A, 3 * A, A, 5 * A, 1, 1, 64, 128, 0.1, None) == S["FA_ERR_ALIAS"]
+    assert lib.fa_fwd(None, None, None, None, None, 1, 1, 0, 128, 0.1, None) == 0  # empty: no-op
+    assert lib.fa_unfused_fwd(A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 1, 64, 128, 0.1, None, 0, None) == \
+        S["FA_ERR_WORKSPACE"]
+
+
+def test_python_binding_type_checks(fa):
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError):  # CPU tensors are refused: there is no CPU path
+        fa.fa_fwd(q, q, q, q.clone(), lse)
+    with pytest.raises(TypeError):
+        fa.fa_fwd(q.float(), q, q, q.clone(), lse)
