@@ -137,117 +137,35 @@ __device__ __forceinline__ void issue_tile(const char* __restrict__ gk, const ch
   }
 }
 
-// Scores of one 32-key sub-tile: S^T[qb] = K_sub Q_block(qb)^T over all of d.
-// kst points at the sub-tile's first key row in LDS.
-template <int D>
-__device__ __forceinline__ void qk_sub(f32x16_t (&s)[2], const bf16x8_t (&qf)[2][Cfg<D>::kKS],
-                                       const LDS_AS char* kst, const int (&koff)[Cfg<D>::kKS]) {
-  using C = Cfg<D>;
-  s[0] = f32x16_t{};
-  s[1] = f32x16_t{};
-#pragma unroll
-  for (int ks = 0; ks < C::kKS; ++ks) {
-    const bf16x8_t a = *(const LDS_AS bf16x8_t*)(kst + koff[ks]);
-    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][ks], s[0], 0, 0, 0);
-    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][ks], s[1], 0, 0, 0);
-  }
+// ---------------------------------------------------------------------------
+// MFMA issue with pinned register classes. The scores S^T live in VGPRs (the
+// softmax reads them with VALU instructions); the output accumulator O^T lives
+// in AGPRs for the whole kernel (only MFMAs and the rare rescale touch it). The
+// compiler does not see these as MFMAs, so the code below keeps the required
+// wait states itself: S is read by VALU code at least 16 MFMAs after it was
+// written, P is written at least one step before the MFMA that reads it, and
+// every VALU access to O^T goes through sync_acc() first.
+// Scores: the Q^T operand (b) stays in AGPRs too, as the MFMA B source.
+__device__ __forceinline__ void mfma_s(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_s0(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_o(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 
-// Key index, within a 32-key sub-tile, of S^T accumulator register i, minus 8g:
-// key = 8g + 16*(i/8) + 4*((i/4)%2) + i%4 (the pi row permutation).
-__device__ __forceinline__ constexpr int key_of_reg(int i) { return 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3); }
-
-// Online-softmax part 1 on one sub-tile (FA1 page, derivation steps 1-2): the row
-// max of the sub-tile, and a new reference max where it exceeds the current one
-// by more than the threshold. Returns whether any row of the wave moved its
-// reference; then alpha = exp2(m_old - m_new) and l has been scaled by it (the
-// caller scales acc once the previous sub-tile's PV product is in). kMasked sets
-// keys >= nvalid (passed as nvalid - 8g) to -inf.
-template <bool kMasked>
-__device__ __forceinline__ bool sub_max(f32x16_t (&s)[2], float (&m)[2], float (&l)[2], float (&alpha)[2], float c,
-                                        int nvalid_minus_8g) {
-  float mt[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float x = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if constexpr (kMasked) {
-        if (key_of_reg(i) >= nvalid_minus_8g) s[qb][i] = -__builtin_inff();
-      }
-      x = fmaxf(x, s[qb][i]);
-    }
-    mt[qb] = pair_max(x) * c;
-  }
-  const bool need = (mt[0] > m[0] + kRescaleThreshold) || (mt[1] > m[1] + kRescaleThreshold);
-  const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
-  if (any) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float mn = fmaxf(m[qb], mt[qb]);
-      alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mn);
-      m[qb] = mn;
-      l[qb] *= alpha[qb];
-    }
-  }
-  return any;
+// Wait states between the last MFMA that wrote an accumulator and VALU reads of it.
+__device__ __forceinline__ void sync_acc(f32x16_t& a, f32x16_t& b) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(a), "+a"(b));
 }
 
-// Online-softmax part 2 (FA1 page, step 1 numerators, step 2 running sum):
-// P~ = exp2(s*c - m) in fp32, l += rowsum(P~), and P~ rounded to bf16 in the
-// B-operand layout of the PV product: p[qb][h] holds accumulator registers 8h..8h+7.
-template <bool kMasked>
-__device__ __forceinline__ void sub_exp(const f32x16_t (&s)[2], const float (&m)[2], float (&l)[2],
-                                        bf16x8_t (&p)[2][2], float c, int nvalid_minus_8g) {
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float negm = -m[qb];
-    float sum = 0.0f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8_t v;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = h * 8 + j;
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][i], c, negm));
-        if constexpr (kMasked) {
-          if (key_of_reg(i) >= nvalid_minus_8g) e = 0.0f;
-        }
-        sum += e;
-        v[j] = (__bf16)e;
-      }
-      p[qb][h] = v;
-    }
-    l[qb] += sum;
-  }
-}
-
-// acc^T[db][qb] += V_sub^T(db) P^T(qb) for one 32-key sub-tile (two 16-key steps).
-// vst points at the sub-tile's first value row in LDS.
-template <int D>
-__device__ __forceinline__ void pv_sub(f32x16_t (&acc)[Cfg<D>::kDB][2], const bf16x8_t (&p)[2][2],
-                                       const LDS_AS char* vst, const int (&voff)[Cfg<D>::kDB][2]) {
-  using C = Cfg<D>;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int db = 0; db < C::kDB; ++db) {
-      const LDS_AS char* base = vst + h * 16 * C::kRowBytes;
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(base + voff[db][0]));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(base + voff[db][1]));
-      const bf16x8_t a = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
-                                                 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[0][h], acc[db][0], 0, 0, 0);
-      acc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[1][h], acc[db][1], 0, 0, 0);
-    }
-  }
-}
-
-// acc *= alpha, in place in AGPRs, when flag != 0. VALU cannot read AGPRs, so each
-// element goes through a VGPR. The branch lives inside the asm so that the
+// acc *= alpha, in place in AGPRs, when flag != 0 (VALU cannot read AGPRs, so
+// each element goes through a VGPR). The branch lives inside the asm so that the
 // compiler sees one unconditional definition of acc and keeps it in the same
-// AGPRs across the loop. The s_nops cover the wait states after the MFMA that
-// last wrote acc and before the next MFMA reads it.
+// AGPRs. The s_nops cover the wait states after the MFMA that last wrote acc and
+// before the next MFMA reads it.
 __device__ __forceinline__ void scale_agpr_if(f32x16_t& a, float alpha, unsigned flag) {
   float t;
   asm volatile(
@@ -279,38 +197,243 @@ __device__ __forceinline__ void scale_agpr_if(f32x16_t& a, float alpha, unsigned
       : "scc");
 }
 
-// One software-pipeline step over 32-key sub-tiles: the PV product of sub-tile u
-// (P operand cur) overlaps the scores and exp2 terms of sub-tile u+1 (into nxt).
-// When sub-tile u+1 starts a new K/V tile, wait for its loads, synchronise the
-// workgroup and start loading the following tile into the stage that the tile
-// before u's has freed. kMasked: sub-tile u+1 is the ragged last one.
-template <int D, bool kMasked>
-__device__ __forceinline__ void pipeline_step(int u, int T, int N, const char* gk, const char* gv, LDS_AS char* lds,
-                                              int wave, int lane, f32x16_t (&s)[2],
-                                              const bf16x8_t (&qf)[2][Cfg<D>::kKS], const int (&koff)[Cfg<D>::kKS],
-                                              const int (&voff)[Cfg<D>::kDB][2], float (&m)[2], float (&l)[2],
-                                              f32x16_t (&acc)[Cfg<D>::kDB][2], const bf16x8_t (&cur)[2][2],
-                                              bf16x8_t (&nxt)[2][2], float c, int nv8) {
+// Key index, within a 32-key sub-tile, of S^T accumulator register i, minus 8g:
+// key = 8g + 16*(i/8) + 4*((i/4)%2) + i%4 (the pi row permutation).
+__device__ __forceinline__ constexpr int key_of_reg(int i) { return 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3); }
+
+template <int I, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
+// State of one wave's 64 query rows (two 32-row MFMA column blocks qb = 0, 1).
+template <int D>
+struct Wave {
   using C = Cfg<D>;
-  if (u & 1) {
-    const int t = (u + 1) >> 1;
-    wait_vmem();
-    __syncthreads();
-    if (t + 1 < T) issue_tile<D>(gk, gv, t + 1, N, lds + ((t + 1) % C::kStages) * C::kStageBytes, wave, lane);
-  }
-  const int un = u + 1;
-  qk_sub<D>(s, qf, lds + ((un >> 1) % C::kStages) * C::kStageBytes + (un & 1) * 32 * C::kRowBytes, koff);
-  float alpha[2] = {1.0f, 1.0f};
-  const bool rescale = sub_max<kMasked>(s, m, l, alpha, c, nv8);
-  pv_sub<D>(acc, cur, lds + ((u >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + (u & 1) * 32 * C::kRowBytes,
-            voff);
-  sub_exp<kMasked>(s, m, l, nxt, c, nv8);
-  const unsigned flag = __builtin_amdgcn_readfirstlane(rescale ? 1u : 0u);
+  bf16x8_t qf[2][C::kKS];     // Q^T operands (AGPRs)
+  int koff[C::kKS];           // LDS byte offsets of this lane's K operand reads
+  int voff[C::kDB][2];        // ... and of its V transposing reads
+  f32x16_t acc[C::kDB][2];    // O^T accumulator (AGPRs)
+  float m[2];                 // reference max, log2 units
+  float l[2];                 // this lane's part of the running sum
+  bf16x8_t vpre[4];           // V^T operands of the next step's first PV slots, read ahead
+  bool rescale;               // the reference max moved in the last softmax: scale acc
+  float alpha[2];             // ... by exp2(m_old - m_new) before the next PV product
+};
+
+// One pipeline step j over 32-key sub-tiles (FA1 page, derivation steps 1-5, with
+// the division by l deferred to the end). The matrix cores add sub-tile j-1's PV
+// product (kPV) and then compute the scores of sub-tile j+1 (kQK), while the VALU
+// does the online softmax of sub-tile j (kExp: steps 1-2 of the derivation,
+// scores in scur, exp2 terms into pcur), so no MFMA depends on a VALU result of
+// the same step. Issue order is fixed by sched_barrier fences: MFMA slot s is
+// followed by its share of the softmax work and by LDS reads issued ahead of use.
+// With kOneS the softmax finishes during the PV slots, so the scores of j+1 can
+// overwrite those of j (scur and snxt may be the same registers); otherwise it is
+// spread over all slots and scur/snxt must differ. kMasked: sub-tile j is the
+// ragged last one (keys >= nvalid, passed as nvalid - 8g, are masked).
+template <int D, bool kPV, bool kExp, bool kQK, bool kMasked, bool kOneS>
+__device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, const char* gk, const char* gv,
+                                              LDS_AS char* lds, int wave, int lane, f32x16_t (&scur)[2],
+                                              f32x16_t (&snxt)[2], const bf16x8_t (&pprev)[2][2],
+                                              bf16x8_t (&pcur)[2][2], float c, int nv8) {
+  using C = Cfg<D>;
+  constexpr int KS = C::kKS, DB = C::kDB;
+  constexpr int NPV = kPV ? 4 * DB : 0;        // MFMA slots of the PV product (first)
+  constexpr int NS = NPV + (kQK ? 2 * KS : 0);  // all MFMA slots
+  constexpr int NI = kExp ? 5 + 32 : 0;        // softmax work items
+  constexpr int NVS = kOneS ? NPV : NS;        // slots that carry softmax work
+  constexpr int NPAIR = 2 * DB;                // V^T operand pairs (h, db) of a PV product
+  constexpr int kVPre = 4;                     // pairs read in the previous step
+  constexpr int kVLead = 4;                    // other pairs: read this many pairs ahead
+  constexpr int kKStart = NPV > 8 ? NPV - 8 : 0;  // slot where K operand reads start
+  static_assert(NPAIR >= kVPre, "prefetch depth");
+
+  if constexpr (kPV) {
+    // The previous softmax moved the reference max (uniform branch, rarely
+    // taken): bring the PV products accumulated so far to the new reference.
+    if (w.rescale) {
 #pragma unroll
-  for (int db = 0; db < C::kDB; ++db) {
-    scale_agpr_if(acc[db][0], alpha[0], flag);
-    scale_agpr_if(acc[db][1], alpha[1], flag);
+      for (int db = 0; db < DB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
+      // One fragment at a time: each asm ties the finished fragment to the next
+      // one, so the compiler cannot pull all 128 values into VGPRs at once.
+#pragma unroll
+      for (int f = 0; f < 2 * DB; ++f) {
+        w.acc[f >> 1][f & 1] *= w.alpha[f & 1];
+        if (f + 1 < 2 * DB) asm volatile("" : "+a"(w.acc[f >> 1][f & 1]), "+a"(w.acc[(f + 1) >> 1][(f + 1) & 1]));
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
+    }
   }
+  if constexpr (kQK) {
+    if (j & 1) {  // sub-tile j+1 opens K/V tile t: wait for it, then start loading tile t+1
+      const int t = (j + 1) >> 1;
+      wait_vmem();
+      __syncthreads();
+      if (t + 1 < T) issue_tile<D>(gk, gv, t + 1, N, lds + ((t + 1) % C::kStages) * C::kStageBytes, wave, lane);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const LDS_AS char* kst = nullptr;
+  const LDS_AS char* vst = nullptr;
+  const LDS_AS char* vnx = nullptr;  // V of sub-tile j, read ahead for the next step
+  if constexpr (kQK) kst = lds + (((j + 1) >> 1) % C::kStages) * C::kStageBytes + ((j + 1) & 1) * 32 * C::kRowBytes;
+  if constexpr (kPV)
+    vst = lds + (((j - 1) >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + ((j - 1) & 1) * 32 * C::kRowBytes;
+  if constexpr (kExp) vnx = lds + ((j >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + (j & 1) * 32 * C::kRowBytes;
+
+  auto read_v = [&](const LDS_AS char* base, int pr) -> bf16x8_t {
+    const int h = pr / DB, db = pr % DB;
+    const LDS_AS char* b = base + h * 16 * C::kRowBytes;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(b + w.voff[db][0]));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(b + w.voff[db][1]));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4,
+                                   5, 6, 7);
+  };
+  bf16x8_t kf[KS];
+  bf16x8_t vf[NPAIR];
+  auto load_k = [&](auto ks_tag) {
+    constexpr int ks = decltype(ks_tag)::value;
+    if constexpr (kQK && ks < KS) kf[ks] = *(const LDS_AS bf16x8_t*)(kst + w.koff[ks]);
+  };
+  auto load_v = [&](auto p_tag) {
+    constexpr int p = decltype(p_tag)::value;
+    if constexpr (kPV && p >= kVPre && p < NPAIR) vf[p] = read_v(vst, p);
+  };
+  auto prefetch_next = [&](auto p_tag) {
+    constexpr int p = decltype(p_tag)::value;
+    if constexpr (kExp && p < kVPre) w.vpre[p] = read_v(vnx, p);
+  };
+  if constexpr (kPV) {
+#pragma unroll
+    for (int p = 0; p < kVPre; ++p) vf[p] = w.vpre[p];
+  }
+
+  // Wait states between the MFMAs that wrote scur (end of the previous step) and
+  // the VALU reads of it below.
+  if constexpr (kExp) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(scur[0]), "+v"(scur[1]));
+
+  // Softmax state of this step.
+  float x[2] = {-__builtin_inff(), -__builtin_inff()};
+  float alpha[2] = {1.0f, 1.0f};
+  float sum[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+  bool any = false;
+  auto valu_item = [&](auto it_tag) {
+    constexpr int it = decltype(it_tag)::value;
+    if constexpr (it < 4) {  // partial row max over 8 registers
+      constexpr int qb = it / 2, i0 = (it % 2) * 8;
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i) {
+        if constexpr (kMasked) {
+          if (key_of_reg(i) >= nv8) scur[qb][i] = -__builtin_inff();
+        }
+        x[qb] = fmaxf(x[qb], scur[qb][i]);
+      }
+    } else if constexpr (it == 4) {  // tile max, reference update, l rescale
+      float mt[2];
+      bool need = false;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        mt[qb] = pair_max(x[qb]) * c;
+        need |= mt[qb] > w.m[qb] + kRescaleThreshold;
+      }
+      any = __builtin_amdgcn_ballot_w64(need) != 0;
+      // Branch-free: without a move, mt - inf = -inf leaves the reference as is.
+      const float off = any ? 0.0f : __builtin_inff();
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mn = fmaxf(w.m[qb], mt[qb] - off);
+        alpha[qb] = __builtin_amdgcn_exp2f(w.m[qb] - mn);
+        w.m[qb] = mn;
+        w.l[qb] *= alpha[qb];
+      }
+    } else {  // one exp2 term: register i of block qb
+      constexpr int e = it - 5, qb = e / 16, i = e % 16;
+      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[qb][i], c, -w.m[qb]));
+      if constexpr (kMasked) {
+        if (key_of_reg(i) >= nv8) pv = 0.0f;
+      }
+      sum[qb][i & 1] += pv;
+      pcur[qb][i >> 3][i & 7] = (__bf16)pv;
+    }
+  };
+  auto finish_softmax = [&]() {
+    if constexpr (kExp) {
+      w.l[0] += sum[0][0] + sum[0][1];
+      w.l[1] += sum[1][0] + sum[1][1];
+      // Before the first PV product acc is zero: nothing to rescale.
+      w.rescale = kPV && any;
+      w.alpha[0] = alpha[0];
+      w.alpha[1] = alpha[1];
+    }
+  };
+  // Reads issued before the first slot.
+  static_for<0, NPAIR>([&](auto p_tag) {
+    constexpr int p = decltype(p_tag)::value;
+    if constexpr (2 * (p - kVLead) < 0) load_v(p_tag);
+  });
+  if constexpr (kKStart == 0) static_for<0, 3>(load_k);
+  if constexpr (NVS == 0) {  // no slot carries softmax work: do it before any MFMA
+    static_for<0, NI>(valu_item);
+    finish_softmax();
+  }
+
+  static_for<0, NS>([&](auto s_tag) {
+    constexpr int s = decltype(s_tag)::value;
+    if constexpr (s < NPV) {
+      constexpr int pr = s / 2, qb = s % 2;
+      constexpr int h = pr / DB, db = pr % DB;
+      mfma_o(w.acc[db][qb], vf[pr], pprev[qb][h]);
+      // V pairs kVLead pairs ahead of their first slot.
+      static_for<0, NPAIR>([&](auto p_tag) {
+        constexpr int p = decltype(p_tag)::value;
+        if constexpr (2 * (p - kVLead) == s) load_v(p_tag);
+      });
+    } else {
+      constexpr int ks = (s - NPV) / 2, qb = (s - NPV) % 2;
+      if constexpr (ks == 0) {
+        mfma_s0(snxt[qb], kf[ks], w.qf[qb][ks]);
+      } else {
+        mfma_s(snxt[qb], kf[ks], w.qf[qb][ks]);
+      }
+      // read ahead the next step's first V pairs
+      if constexpr (qb == 1 && ks < kVPre) prefetch_next(std::integral_constant<int, ks>{});
+    }
+    // K operand reads: three k-steps ahead, starting kKStart slots in.
+    if constexpr (kQK && s >= kKStart && (s - kKStart) % 2 == 0) {
+      constexpr int n = (s - kKStart) / 2;  // n-th K read of this step, needed at slot NPV + 2n
+      if constexpr (kKStart > 0) {
+        load_k(std::integral_constant<int, n>{});
+      } else {
+        load_k(std::integral_constant<int, n + 3>{});
+      }
+    }
+    // This slot's share of the softmax work, pinned to the slot: the empty asm
+    // consumes the P operands produced so far, so later passes cannot sink the
+    // exp2 work past the slot.
+    if constexpr (s < NVS) {
+      constexpr int i0 = (s * NI) / NVS, i1 = ((s + 1) * NI) / NVS;
+      static_for<i0, i1>(valu_item);
+      if constexpr (i1 > 5) {
+        constexpr int e1 = i1 - 5;  // exp items done so far
+        if constexpr (e1 > 0) asm volatile("" : "+v"(pcur[0][0]));
+        if constexpr (e1 > 8) asm volatile("" : "+v"(pcur[0][1]));
+        if constexpr (e1 > 16) asm volatile("" : "+v"(pcur[1][0]));
+        if constexpr (e1 > 24) asm volatile("" : "+v"(pcur[1][1]));
+      }
+    }
+    if constexpr (s == NVS - 1) finish_softmax();
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  if constexpr (kExp && !kQK) {  // no score slots: read the next step's V operands now
+    static_for<0, kVPre>(prefetch_next);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D>
@@ -338,96 +461,121 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   // Start streaming K/V tile 0 while Q is loaded.
   issue_tile<D>(gk, gv, 0, N, lds, wave, lane);
 
+  Wave<D> w;
   // Q^T operand fragments: lane holds query q0 + qb*32 + lane%32, d = ks*16 + g*8 .. +8.
-  bf16x8_t qf[2][C::kKS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = q0 + qb * 32 + (lane & 31);
     const bf16x8_t* src = (const bf16x8_t*)(q + head_off + (size_t)min(row, N - 1) * D + g * 8);
 #pragma unroll
     for (int ks = 0; ks < C::kKS; ++ks) {
-      bf16x8_t x = src[ks * 2];
-      if (row >= N) x = bf16x8_t{};
-      qf[qb][ks] = x;
+      bf16x8_t xq = src[ks * 2];
+      if (row >= N) xq = bf16x8_t{};
+      w.qf[qb][ks] = xq;
     }
   }
-
+  // Wait states between the AGPR writes of Q^T and the first MFMA that reads them.
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ++ks) asm volatile("s_nop 1" : "+a"(w.qf[0][ks]), "+a"(w.qf[1][ks]));
+  asm volatile("s_nop 7" ::: "memory");
   // Per-lane LDS byte offsets of the operand reads (sub-tile base added later; the
   // swizzle depends on row bits 0-3 only, so 16-row-aligned bases keep it).
-  int koff[C::kKS];
   {
     const int r0 = pi_row(lane & 31);
 #pragma unroll
-    for (int ks = 0; ks < C::kKS; ++ks) koff[ks] = chunk_offset<D>(r0, ks * 2 + g);
+    for (int ks = 0; ks < C::kKS; ++ks) w.koff[ks] = chunk_offset<D>(r0, ks * 2 + g);
   }
-  int voff[C::kDB][2];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int row = 8 * g + 4 * r + ((lane & 15) >> 2);
       const int dcol = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      voff[db][r] = chunk_offset<D>(row, dcol >> 3) + 2 * (dcol & 7);
+      w.voff[db][r] = chunk_offset<D>(row, dcol >> 3) + 2 * (dcol & 7);
     }
   }
-
-  float m[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l[2] = {0.0f, 0.0f};
-  f32x16_t acc[C::kDB][2];
+  w.m[0] = w.m[1] = -__builtin_inff();
+  w.l[0] = w.l[1] = 0.0f;
+  w.rescale = false;
+  w.alpha[0] = w.alpha[1] = 1.0f;
 #pragma unroll
-  for (int db = 0; db < C::kDB; ++db) acc[db][0] = acc[db][1] = f32x16_t{};
+  for (int db = 0; db < C::kDB; ++db) {
+    w.acc[db][0] = f32x16_t{};
+    w.acc[db][1] = f32x16_t{};
+  }
 
   wait_vmem();
   __syncthreads();
   if (T > 1) issue_tile<D>(gk, gv, 1, N, lds + C::kStageBytes, wave, lane);
 
-  // Software pipeline over 32-key sub-tiles (see pipeline_step).
   const int nvalid_last = N - (U - 1) * 32;  // 1..32 keys in the last sub-tile
   const bool ragged = nvalid_last < 32;
   const int nv8 = nvalid_last - 8 * g;
-  f32x16_t s[2];
+  f32x16_t sa[2], sb[2];
   bf16x8_t pa[2][2], pb[2][2];
+
+  // Scores of sub-tile 0.
   {
-    float alpha[2];
-    qk_sub<D>(s, qf, lds, koff);
-    if (U == 1 && ragged) {
-      sub_max<true>(s, m, l, alpha, c, nv8);
-      sub_exp<true>(s, m, l, pa, c, nv8);
-    } else {
-      sub_max<false>(s, m, l, alpha, c, nv8);
-      sub_exp<false>(s, m, l, pa, c, nv8);
-    }
-  }
-  int u = 0;
-  for (; u + 2 < U; ++u) {
-    pipeline_step<D, false>(u, T, N, gk, gv, lds, wave, lane, s, qf, koff, voff, m, l, acc, pa, pb, c, nv8);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      pa[qb][0] = pb[qb][0];
-      pa[qb][1] = pb[qb][1];
+    for (int ks = 0; ks < C::kKS; ++ks) {
+      const bf16x8_t kfr = *(const LDS_AS bf16x8_t*)(lds + w.koff[ks]);
+      if (ks == 0) {
+        mfma_s0(sa[0], kfr, w.qf[0][ks]);
+        mfma_s0(sa[1], kfr, w.qf[1][ks]);
+      } else {
+        mfma_s(sa[0], kfr, w.qf[0][ks]);
+        mfma_s(sa[1], kfr, w.qf[1][ks]);
+      }
     }
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(sa[0]), "+v"(sa[1]));
   }
-  if (u + 1 < U) {  // u == U-2: the next sub-tile is the last one
-    if (ragged) {
-      pipeline_step<D, true>(u, T, N, gk, gv, lds, wave, lane, s, qf, koff, voff, m, l, acc, pa, pb, c, nv8);
+
+  // Step j: PV of j-1, softmax of j, scores of j+1. d = 128 keeps one score
+  // buffer (the softmax of j ends before the scores of j+1 are written); d = 64
+  // alternates two and spreads the softmax over every slot.
+  constexpr bool kOneS = D == 128;
+#define FA_STEP(PV, EXP, QK, MASK, J, SC, SN, PP, PC)                                                   \
+  pipeline_step<D, PV, EXP, QK, MASK, kOneS>(w, J, T, N, gk, gv, lds, wave, lane, (kOneS ? sa : SC), \
+                                             (kOneS ? sa : SN), PP, PC, c, nv8)
+  if (U == 1) {
+    if (ragged) FA_STEP(false, true, false, true, 0, sa, sb, pb, pa);
+    else FA_STEP(false, true, false, false, 0, sa, sb, pb, pa);
+  } else {
+    FA_STEP(false, true, true, false, 0, sa, sb, pb, pa);
+  }
+  // Full steps j = 1 .. U-2, two per iteration.
+  int j = 1;
+  for (; j + 1 <= U - 2; j += 2) {
+    FA_STEP(true, true, true, false, j, sb, sa, pa, pb);
+    FA_STEP(true, true, true, false, j + 1, sa, sb, pb, pa);
+  }
+  if (j <= U - 2) {  // one more full step, j odd
+    FA_STEP(true, true, true, false, j, sb, sa, pa, pb);
+    ++j;
+  }
+  // j == U - 1 when U >= 2: PV of U-2 and softmax of the last sub-tile; then step U:
+  // PV of the last sub-tile.
+  if (U >= 2) {
+    if (j & 1) {
+      if (ragged) FA_STEP(true, true, false, true, j, sb, sa, pa, pb);
+      else FA_STEP(true, true, false, false, j, sb, sa, pa, pb);
+      FA_STEP(true, false, false, false, j + 1, sa, sb, pb, pa);
     } else {
-      pipeline_step<D, false>(u, T, N, gk, gv, lds, wave, lane, s, qf, koff, voff, m, l, acc, pa, pb, c, nv8);
+      if (ragged) FA_STEP(true, true, false, true, j, sa, sb, pb, pa);
+      else FA_STEP(true, true, false, false, j, sa, sb, pb, pa);
+      FA_STEP(true, false, false, false, j + 1, sb, sa, pa, pb);
     }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      pa[qb][0] = pb[qb][0];
-      pa[qb][1] = pb[qb][1];
-    }
-    ++u;
+  } else {
+    FA_STEP(true, false, false, false, 1, sb, sa, pa, pb);
   }
-  // Last sub-tile: PV only.
-  pv_sub<D>(acc, pa, lds + ((u >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + (u & 1) * 32 * C::kRowBytes,
-            voff);
+#undef FA_STEP
 
   // Epilogue: O = acc / l (bf16, nearest-even), LSE = ln2 * (m + log2 l).
 #pragma unroll
+  for (int db = 0; db < C::kDB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
+#pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lsum = pair_sum(l[qb]);
+    const float lsum = pair_sum(w.l[qb]);
     const float inv = 1.0f / lsum;
     const int row = q0 + qb * 32 + (lane & 31);
     if (row < N) {
@@ -436,13 +584,13 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
       for (int db = 0; db < C::kDB; ++db) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4_t w;
+          bf16x4_t wv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][qb][i4 * 4 + e] * inv);
-          *(bf16x4_t*)(dst + db * 32 + 8 * i4 + 4 * g) = w;
+          for (int e = 0; e < 4; ++e) wv[e] = (__bf16)(w.acc[db][qb][i4 * 4 + e] * inv);
+          *(bf16x4_t*)(dst + db * 32 + 8 * i4 + 4 * g) = wv;
         }
       }
-      if (g == 0) lse[(size_t)bh * N + row] = kLn2 * (m[qb] + log2f(lsum));
+      if (g == 0) lse[(size_t)bh * N + row] = kLn2 * (w.m[qb] + log2f(lsum));
     }
   }
 }
