@@ -82,6 +82,62 @@ def cpu_baseline(w, q, k, v, target_s: float = 10.0, max_heads: int = 32):
     }
 
 
+def _read_counter_csv(path):
+    """(kernel name, counter name) -> list of per-dispatch values, in dispatch order."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            key = (row["Kernel_Name"], row["Counter_Name"])
+            out.setdefault(key, []).append((int(row["Dispatch_Id"]), float(row["Counter_Value"])))
+    return {k: [v for _, v in sorted(vals)] for k, vals in out.items()}
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel by what the
+    same counters read for the plain copy of ``copy_bytes`` bytes in the same run."""
+    import attn_inputs
+
+    w = attn_inputs.HEADLINE if workload is None else attn_inputs.WORKLOAD_BY_NAME[workload]
+    fetch = _read_counter_csv(fetch_csv)
+    write = _read_counter_csv(write_csv)
+
+    def pick(table, counter, pred):
+        vals = [v for (k, c), vs in table.items() if c == counter and pred(k) for v in vs]
+        if not vals:
+            raise SystemExit(f"no {counter} values for the requested kernel in the CSV")
+        return vals
+
+    is_fa = lambda k: "fa_fwd_kernel" in k
+    is_copy = lambda k: "fa_fwd_kernel" not in k and "unf_" not in k
+    copy_fetch = pick(fetch, "FETCH_SIZE", is_copy)[0] * 1024.0
+    copy_write = pick(write, "WRITE_SIZE", is_copy)[0] * 1024.0
+    f_scale = copy_bytes / copy_fetch
+    w_scale = copy_bytes / copy_write
+    fa_fetch = pick(fetch, "FETCH_SIZE", is_fa)
+    fa_write = pick(write, "WRITE_SIZE", is_fa)
+    fetch_b = sum(fa_fetch) / len(fa_fetch) * 1024.0 * f_scale
+    write_b = sum(fa_write) / len(fa_write) * 1024.0 * w_scale
+    rec = {
+        "workload": w.name,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "hbm_bytes_per_launch": round(fetch_b + write_b),
+        "fetch_bytes_per_launch": round(fetch_b),
+        "write_bytes_per_launch": round(write_b),
+        "min_hbm_bytes_per_launch": w.min_hbm_bytes,
+        "ratio_to_min": round((fetch_b + write_b) / w.min_hbm_bytes, 4),
+        "copy_calibration_bytes": copy_bytes,
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "fetch_kib_raw_per_launch": [round(v, 1) for v in fa_fetch],
+        "write_kib_raw_per_launch": [round(v, 1) for v in fa_write],
+    }
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{w.name}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,11 +148,21 @@ def main():
     ap.add_argument("--unfused", action="store_true", help="time the three-kernel baseline instead")
     ap.add_argument("--launches-only", action="store_true",
                     help="only run warmup+steps launches (for profilers), print nothing but the JSON line")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run one plain device-to-device copy of BYTES bytes (a known-size reference "
+                         "dispatch for the FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: read two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --copy-calibration run and write profiles/fa_fwd_<workload>_traffic.json")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_calibration)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the forward shards over heads with no exchange; see DESIGN.md).", file=sys.stderr)
+              "(the forward shards over heads with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
 
     threads = str(len(os.sched_getaffinity(0)))
@@ -118,6 +184,13 @@ def main():
     ws = None
     if args.unfused:
         ws = torch.empty(fa.fa_unfused_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def launch():
         if args.unfused:

@@ -116,24 +116,49 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Byte offset, within a K or V tile in global memory, of the 16 bytes that lane
+// `lane` of wave `wave` copies with its i-th direct-to-LDS load. Slot p (16 bytes,
+// lane-consecutive per instruction) holds row p / kChunks and physical chunk
+// p % kChunks, i.e. logical chunk (p % kChunks) ^ swz(row).
+template <int D>
+__device__ __forceinline__ unsigned tile_load_offset(int wave, int lane, int i, int* row_out) {
+  using C = Cfg<D>;
+  const int p = (wave * C::kLoadsPerWave + i) * 64 + lane;
+  const int row = p / C::kChunks;
+  const int chunk = (p % C::kChunks) ^ swz<D>(row);
+  *row_out = row;
+  return (unsigned)(row * (D * 2) + chunk * 16);
+}
+
 // Issue the direct-to-LDS loads of K and V tile t of one head into `stage`.
-// Slot p (16 bytes, lane-consecutive per instruction) holds row p / kChunks and
-// physical chunk p % kChunks, i.e. logical chunk (p % kChunks) ^ swz(row). Rows
+// gofs holds this lane's tile_load_offset values. In the last, partial tile rows
 // past N re-read row N-1: finite data whose scores are masked to -inf.
 template <int D>
 __device__ __forceinline__ void issue_tile(const char* __restrict__ gk, const char* __restrict__ gv, int t, int N,
-                                           LDS_AS char* stage, int wave, int lane) {
+                                           LDS_AS char* stage, int wave, int lane,
+                                           const unsigned* gofs) {
   using C = Cfg<D>;
+  const size_t tb = (size_t)t * C::kBC * (D * 2);
+  if ((t + 1) * C::kBC <= N) {
+    const char* tk = gk + tb;
+    const char* tv = gv + tb;
 #pragma unroll
-  for (int i = 0; i < C::kLoadsPerWave; ++i) {
-    const int ii = wave * C::kLoadsPerWave + i;
-    const int p = ii * 64 + lane;
-    const int row = p / C::kChunks;
-    const int chunk = (p % C::kChunks) ^ swz<D>(row);
-    const int grow = min(t * C::kBC + row, N - 1);
-    const size_t goff = (size_t)grow * (D * 2) + (size_t)chunk * 16;
-    __builtin_amdgcn_global_load_lds(gk + goff, (LDS_AS void*)(stage + ii * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gv + goff, (LDS_AS void*)(stage + C::kTileBytes + ii * 1024), 16, 0, 0);
+    for (int i = 0; i < C::kLoadsPerWave; ++i) {
+      const int ii = wave * C::kLoadsPerWave + i;
+      __builtin_amdgcn_global_load_lds(tk + gofs[i], (LDS_AS void*)(stage + ii * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(tv + gofs[i], (LDS_AS void*)(stage + C::kTileBytes + ii * 1024), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::kLoadsPerWave; ++i) {
+      const int ii = wave * C::kLoadsPerWave + i;
+      int row;
+      const unsigned off = tile_load_offset<D>(wave, lane, i, &row);
+      const int grow = min(t * C::kBC + row, N - 1);
+      const size_t goff = (size_t)grow * (D * 2) + (off - (unsigned)row * (D * 2));
+      __builtin_amdgcn_global_load_lds(gk + goff, (LDS_AS void*)(stage + ii * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gv + goff, (LDS_AS void*)(stage + C::kTileBytes + ii * 1024), 16, 0, 0);
+    }
   }
 }
 
@@ -214,8 +239,9 @@ template <int D>
 struct Wave {
   using C = Cfg<D>;
   bf16x8_t qf[2][C::kKS];     // Q^T operands (AGPRs)
-  int koff[C::kKS];           // LDS byte offsets of this lane's K operand reads
-  int voff[C::kDB][2];        // ... and of its V transposing reads
+  unsigned koff[C::kKS];      // LDS addresses of this lane's K operand reads (stage 0, sub-tile 0)
+  unsigned voff[C::kDB][2];   // ... and of its V transposing reads (tile base excluded)
+  unsigned gofs[C::kLoadsPerWave];  // this lane's tile_load_offset values
   f32x16_t acc[C::kDB][2];    // O^T accumulator (AGPRs)
   float m[2];                 // reference max, log2 units
   float l[2];                 // this lane's part of the running sum
@@ -274,24 +300,28 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       const int t = (j + 1) >> 1;
       wait_vmem();
       __syncthreads();
-      if (t + 1 < T) issue_tile<D>(gk, gv, t + 1, N, lds + ((t + 1) % C::kStages) * C::kStageBytes, wave, lane);
+      if (t + 1 < T)
+        issue_tile<D>(gk, gv, t + 1, N, lds + ((t + 1) % C::kStages) * C::kStageBytes, wave, lane, w.gofs);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  const LDS_AS char* kst = nullptr;
-  const LDS_AS char* vst = nullptr;
-  const LDS_AS char* vnx = nullptr;  // V of sub-tile j, read ahead for the next step
-  if constexpr (kQK) kst = lds + (((j + 1) >> 1) % C::kStages) * C::kStageBytes + ((j + 1) & 1) * 32 * C::kRowBytes;
-  if constexpr (kPV)
-    vst = lds + (((j - 1) >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + ((j - 1) & 1) * 32 * C::kRowBytes;
-  if constexpr (kExp) vnx = lds + ((j >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + (j & 1) * 32 * C::kRowBytes;
+  // Byte offsets (uniform, SGPR) of this step's sub-tiles from the LDS base: K of
+  // j+1, V of j-1, and V of j (read ahead for the next step).
+  // readfirstlane: one scalar value each, so every operand address is one v_add.
+  const unsigned kst = __builtin_amdgcn_readfirstlane(
+      kQK ? (unsigned)((((j + 1) >> 1) % C::kStages) * C::kStageBytes + ((j + 1) & 1) * 32 * C::kRowBytes) : 0u);
+  const unsigned vst = __builtin_amdgcn_readfirstlane(
+      kPV ? (unsigned)((((j - 1) >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + ((j - 1) & 1) * 32 * C::kRowBytes)
+          : 0u);
+  const unsigned vnx = __builtin_amdgcn_readfirstlane(
+      kExp ? (unsigned)(((j >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + (j & 1) * 32 * C::kRowBytes) : 0u);
 
-  auto read_v = [&](const LDS_AS char* base, int pr) -> bf16x8_t {
+  auto read_v = [&](unsigned base, int pr) -> bf16x8_t {
     const int h = pr / DB, db = pr % DB;
-    const LDS_AS char* b = base + h * 16 * C::kRowBytes;
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(b + w.voff[db][0]));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(b + w.voff[db][1]));
+    const unsigned b = base + h * 16 * C::kRowBytes;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(w.voff[db][0] + b));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(w.voff[db][1] + b));
     return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4,
                                    5, 6, 7);
   };
@@ -299,7 +329,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   bf16x8_t vf[NPAIR];
   auto load_k = [&](auto ks_tag) {
     constexpr int ks = decltype(ks_tag)::value;
-    if constexpr (kQK && ks < KS) kf[ks] = *(const LDS_AS bf16x8_t*)(kst + w.koff[ks]);
+    if constexpr (kQK && ks < KS) kf[ks] = *(const LDS_AS bf16x8_t*)(uintptr_t)(w.koff[ks] + kst);
   };
   auto load_v = [&](auto p_tag) {
     constexpr int p = decltype(p_tag)::value;
@@ -322,6 +352,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   float x[2] = {-__builtin_inff(), -__builtin_inff()};
   float alpha[2] = {1.0f, 1.0f};
   float sum[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+  float peven[2];  // even-register exp2 term waiting for its odd partner
   bool any = false;
   auto valu_item = [&](auto it_tag) {
     constexpr int it = decltype(it_tag)::value;
@@ -359,7 +390,17 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
         if (key_of_reg(i) >= nv8) pv = 0.0f;
       }
       sum[qb][i & 1] += pv;
-      pcur[qb][i >> 3][i & 7] = (__bf16)pv;
+      if constexpr ((i & 1) == 0) {
+        peven[qb] = pv;
+      } else {  // registers i-1, i -> one packed bf16 pair (v_cvt_pk_bf16_f32, nearest-even)
+        typedef float f32x2_t __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+        const bf16x2_t pr = __builtin_convertvector((f32x2_t){peven[qb], pv}, bf16x2_t);
+        u32x4_t words = __builtin_bit_cast(u32x4_t, pcur[qb][i >> 3]);
+        words[(i & 7) >> 1] = __builtin_bit_cast(unsigned, pr);
+        pcur[qb][i >> 3] = __builtin_bit_cast(bf16x8_t, words);
+      }
     }
   };
   auto finish_softmax = [&]() {
@@ -443,10 +484,12 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
               float c /* scale * log2(e) */) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
-  LDS_AS char* lds = (LDS_AS char*)smem;
+  // The LDS base as a scalar: every LDS address below is a scalar offset plus at
+  // most one per-lane term.
+  LDS_AS char* lds = (LDS_AS char*)(uintptr_t)__builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(LDS_AS char*)smem);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5;  // which half of the wave
   const int logical = remap_xcd(blockIdx.x, total_tiles);
   const int bh = logical / tiles_per_head;
@@ -458,10 +501,15 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   const int U = (N + 31) / 32;              // 32-key sub-tiles processed by the pipeline
   const int q0 = qtile * C::kBR + wave * C::kRowsPerWave;
 
-  // Start streaming K/V tile 0 while Q is loaded.
-  issue_tile<D>(gk, gv, 0, N, lds, wave, lane);
-
   Wave<D> w;
+#pragma unroll
+  for (int i = 0; i < C::kLoadsPerWave; ++i) {
+    int row;
+    w.gofs[i] = tile_load_offset<D>(wave, lane, i, &row);
+  }
+  // Start streaming K/V tile 0 while Q is loaded.
+  issue_tile<D>(gk, gv, 0, N, lds, wave, lane, w.gofs);
+
   // Q^T operand fragments: lane holds query q0 + qb*32 + lane%32, d = ks*16 + g*8 .. +8.
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -480,10 +528,11 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   asm volatile("s_nop 7" ::: "memory");
   // Per-lane LDS byte offsets of the operand reads (sub-tile base added later; the
   // swizzle depends on row bits 0-3 only, so 16-row-aligned bases keep it).
+  const unsigned lds_base = (unsigned)(uintptr_t)lds;
   {
     const int r0 = pi_row(lane & 31);
 #pragma unroll
-    for (int ks = 0; ks < C::kKS; ++ks) w.koff[ks] = chunk_offset<D>(r0, ks * 2 + g);
+    for (int ks = 0; ks < C::kKS; ++ks) w.koff[ks] = lds_base + chunk_offset<D>(r0, ks * 2 + g);
   }
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) {
@@ -491,7 +540,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
     for (int r = 0; r < 2; ++r) {
       const int row = 8 * g + 4 * r + ((lane & 15) >> 2);
       const int dcol = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      w.voff[db][r] = chunk_offset<D>(row, dcol >> 3) + 2 * (dcol & 7);
+      w.voff[db][r] = lds_base + chunk_offset<D>(row, dcol >> 3) + 2 * (dcol & 7);
     }
   }
   w.m[0] = w.m[1] = -__builtin_inff();
@@ -506,7 +555,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
 
   wait_vmem();
   __syncthreads();
-  if (T > 1) issue_tile<D>(gk, gv, 1, N, lds + C::kStageBytes, wave, lane);
+  if (T > 1) issue_tile<D>(gk, gv, 1, N, lds + C::kStageBytes, wave, lane, w.gofs);
 
   const int nvalid_last = N - (U - 1) * 32;  // 1..32 keys in the last sub-tile
   const bool ragged = nvalid_last < 32;
@@ -518,7 +567,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   {
 #pragma unroll
     for (int ks = 0; ks < C::kKS; ++ks) {
-      const bf16x8_t kfr = *(const LDS_AS bf16x8_t*)(lds + w.koff[ks]);
+      const bf16x8_t kfr = *(const LDS_AS bf16x8_t*)(uintptr_t)w.koff[ks];
       if (ks == 0) {
         mfma_s0(sa[0], kfr, w.qf[0][ks]);
         mfma_s0(sa[1], kfr, w.qf[1][ks]);
