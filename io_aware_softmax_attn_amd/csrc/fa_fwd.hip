@@ -59,7 +59,8 @@ struct Cfg {
   static constexpr int kRowsPerWave = 64;
   static constexpr int kBR = kWaves * kRowsPerWave;
   static constexpr int kBC = 64;
-  static constexpr int kStages = 3;
+  static constexpr int kStages = 4;     // K/V tiles resident in LDS
+  static constexpr int kAhead = kStages - 2;  // tiles loading while the current one is read
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;  // 16-byte chunks per K/V row
   static constexpr int kTileBytes = kBC * kRowBytes;
@@ -72,15 +73,21 @@ struct Cfg {
   static_assert(kLoadsPerTile % kWaves == 0, "tile loads must split evenly over waves");
 };
 
-// XOR swizzle of the 16-byte chunk index by row, so that the 16 lanes of one
-// ds_read_b128 (16 rows, same chunk) and the 16 lanes of one ds_read_b64_tr_b16
-// (4 consecutive rows x 2 chunks) hit distinct bank groups.
+// XOR swizzle of the 16-byte chunk index by row (bits 0-3 only, so 16-row-aligned
+// sub-tile bases keep it). With 64 banks of 4 bytes an LDS cycle serves 256 bytes:
+//  * a ds_read_b128 quarter-wave reads one logical chunk of 16 different rows; the
+//    swizzle is a bijection on the row's low bits, so the 16 reads land in 16
+//    distinct 16-byte slots of the bank line;
+//  * a ds_read_b64_tr_b16 half-wave reads 4 consecutive rows x 4 chunks (two lane
+//    groups of 16 with chunk bit 1 = 0 and 1); the swizzle varies with the row
+//    only in chunk bits 2-3 (d = 128) or bit 2 and the bank-line half (d = 64), so
+//    the two groups fill disjoint halves and the half-wave covers every slot once.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (D == 128) {
-    return ((row & 7) << 1) | ((row >> 3) & 1);
+    return ((row & 3) << 2) | ((row >> 2) & 3);
   } else {
-    return (row & 6) | ((row >> 3) & 1);
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   }
 }
 
@@ -116,6 +123,29 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier for the K/V pipeline: each wave has waited for its own
+// direct-to-LDS loads (vmcnt), so after s_barrier every wave's share of the tile is
+// in LDS. LDS reads still in flight target stages nobody overwrites here, so no
+// lgkmcnt wait is needed (unlike __syncthreads). The asm memory clobbers keep the
+// compiler from moving LDS accesses across the barrier.
+template <int kOutstanding>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(kOutstanding == 0 || kOutstanding == 4 || kOutstanding == 8, "add the count");
+  if constexpr (kOutstanding == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (kOutstanding == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if constexpr (kOutstanding == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+
+// kOutstanding: this wave's loads of later tiles that may stay in flight (loads
+// complete in issue order, so everything older, i.e. the tile about to be read,
+// has landed).
+template <int kOutstanding>
+__device__ __forceinline__ void tile_barrier() {
+  wait_vmcnt<kOutstanding>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Byte offset, within a K or V tile in global memory, of the 16 bytes that lane
 // `lane` of wave `wave` copies with its i-th direct-to-LDS load. Slot p (16 bytes,
 // lane-consecutive per instruction) holds row p / kChunks and physical chunk
@@ -130,34 +160,53 @@ __device__ __forceinline__ unsigned tile_load_offset(int wave, int lane, int i, 
   return (unsigned)(row * (D * 2) + chunk * 16);
 }
 
+// One 16-byte-per-lane direct global->LDS load (global_load_lds_dwordx4): lane l's
+// 16 bytes land at LDS address lds_addr + 16*l. Issued through asm so that the
+// compiler, which cannot tell that the destination stage is disjoint from the
+// stages being read, does not put a vmcnt(0) wait in front of the next LDS read;
+// the pipeline waits for these loads itself (tile_barrier). M0 carries the LDS
+// address (one wait state between its write and the load).
+__device__ __forceinline__ void dma16(const char* gbase, unsigned voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_abs(const char* gaddr, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_addr), "v"(gaddr)
+               : "memory", "m0");
+}
+
 // Issue the direct-to-LDS loads of K and V tile t of one head into `stage`.
 // gofs holds this lane's tile_load_offset values. In the last, partial tile rows
 // past N re-read row N-1: finite data whose scores are masked to -inf.
 template <int D>
 __device__ __forceinline__ void issue_tile(const char* __restrict__ gk, const char* __restrict__ gv, int t, int N,
-                                           LDS_AS char* stage, int wave, int lane,
-                                           const unsigned* gofs) {
+                                           LDS_AS char* stage, int wave, int lane, const unsigned* gofs) {
   using C = Cfg<D>;
   const size_t tb = (size_t)t * C::kBC * (D * 2);
+  const unsigned sbase = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)stage);
   if ((t + 1) * C::kBC <= N) {
     const char* tk = gk + tb;
     const char* tv = gv + tb;
 #pragma unroll
     for (int i = 0; i < C::kLoadsPerWave; ++i) {
-      const int ii = wave * C::kLoadsPerWave + i;
-      __builtin_amdgcn_global_load_lds(tk + gofs[i], (LDS_AS void*)(stage + ii * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(tv + gofs[i], (LDS_AS void*)(stage + C::kTileBytes + ii * 1024), 16, 0, 0);
+      const unsigned dst = sbase + (unsigned)((wave * C::kLoadsPerWave + i) * 1024);
+      dma16(tk, gofs[i], dst);
+      dma16(tv, gofs[i], dst + C::kTileBytes);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < C::kLoadsPerWave; ++i) {
-      const int ii = wave * C::kLoadsPerWave + i;
+      const unsigned dst = sbase + (unsigned)((wave * C::kLoadsPerWave + i) * 1024);
       int row;
       const unsigned off = tile_load_offset<D>(wave, lane, i, &row);
       const int grow = min(t * C::kBC + row, N - 1);
       const size_t goff = (size_t)grow * (D * 2) + (off - (unsigned)row * (D * 2));
-      __builtin_amdgcn_global_load_lds(gk + goff, (LDS_AS void*)(stage + ii * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(gv + goff, (LDS_AS void*)(stage + C::kTileBytes + ii * 1024), 16, 0, 0);
+      dma16_abs(gk + goff, dst);
+      dma16_abs(gv + goff, dst + C::kTileBytes);
     }
   }
 }
@@ -296,12 +345,17 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     }
   }
   if constexpr (kQK) {
-    if (j & 1) {  // sub-tile j+1 opens K/V tile t: wait for it, then start loading tile t+1
+    if (j & 1) {  // sub-tile j+1 opens K/V tile t: wait for it, then start loading tile t+kAhead
+      static_assert(C::kAhead == 2, "the wait below assumes one later tile in flight");
       const int t = (j + 1) >> 1;
-      wait_vmem();
-      __syncthreads();
-      if (t + 1 < T)
-        issue_tile<D>(gk, gv, t + 1, N, lds + ((t + 1) % C::kStages) * C::kStageBytes, wave, lane, w.gofs);
+      if (t + 1 < T) {
+        tile_barrier<2 * C::kLoadsPerWave>();
+      } else {
+        tile_barrier<0>();
+      }
+      if (t + C::kAhead < T)
+        issue_tile<D>(gk, gv, t + C::kAhead, N, lds + ((t + C::kAhead) % C::kStages) * C::kStageBytes, wave, lane,
+                      w.gofs);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -555,7 +609,9 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
 
   wait_vmem();
   __syncthreads();
-  if (T > 1) issue_tile<D>(gk, gv, 1, N, lds + C::kStageBytes, wave, lane, w.gofs);
+#pragma unroll
+  for (int t = 1; t <= C::kAhead; ++t)
+    if (t < T) issue_tile<D>(gk, gv, t, N, lds + t * C::kStageBytes, wave, lane, w.gofs);
 
   const int nvalid_last = N - (U - 1) * 32;  // 1..32 keys in the last sub-tile
   const bool ragged = nvalid_last < 32;
