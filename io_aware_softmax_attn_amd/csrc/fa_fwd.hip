@@ -6,26 +6,30 @@
 // 是 IO 瓶颈" page, section 5 skeleton: query tiles outer, K/V tiles streamed inner):
 // each workgroup owns one tile of BR query rows of one (b, h) and streams every
 // K/V tile of that head through LDS, keeping per row a running reference max m,
-// a running sum l of exp2 terms and an unnormalised output accumulator; O = acc/l
-// and LSE = ln2 * (m + log2 l) are written once at the end.
+// a running sum l of exp2 terms and an unnormalised output accumulator; O and
+// LSE = ln2 * (m + log2 l) are written once at the end.
 //
 // gfx950 design (not the pages' GPU design):
 //  * Transposed products. The kernel computes S^T = K Q^T and O^T = V^T P^T with
-//    v_mfma_f32_32x32x16_bf16 so that each lane holds one query column: the row
-//    max and row sum are in-lane reductions plus one permlane32 swap, and the
-//    S^T accumulator converts in registers (v_cvt_pk_bf16_f32) straight into the
-//    B operand of the PV product; P never leaves VGPRs.
+//    v_mfma_f32_32x32x16_bf16 so that each lane holds one query column: row max
+//    and row sum are in-lane reductions plus one permlane32 swap, and the S^T
+//    accumulator converts in registers (v_cvt_pk_bf16_f32) straight into the B
+//    operand of the PV product; P never leaves VGPRs.
 //  * The key order inside a 32-key block is permuted (row bits 2 and 3 swapped
 //    when K rows are fed to the MFMA) so that the accumulator layout of S^T
 //    matches the operand layout that ds_read_b64_tr_b16 produces for V^T. The
 //    contraction over keys does not depend on key order.
-//  * 4 waves x 64 query rows per workgroup (BR = 256), 64-key K/V tiles, three
+//  * 4 waves x 64 query rows per workgroup (BR = 256), 64-key K/V tiles, four
 //    LDS stages filled by direct global->LDS 16-byte loads (global_load_lds_dwordx4)
 //    with a XOR swizzle of 16-byte chunks against LDS bank conflicts.
-//  * exp2 with log2(e) folded into the score scale; the rescale of the
-//    accumulator is skipped while the tile max stays within 2^8 of the reference
-//    max (any reference gives the same O and LSE; only the magnitude of the exp2
-//    terms depends on it).
+//  * Software pipeline over 32-key sub-tiles: while the matrix cores run the PV
+//    product of sub-tile j-1 and the scores of j+1, the VALU runs the softmax of j.
+//  * exp2 with log2(e) folded into the score scale. The exp2 terms are formed
+//    against the current reference max without a per-tile max; the reference
+//    moves (and the accumulator is rescaled) only when a row's terms over a
+//    sub-tile sum past 2^16. Any reference gives the same O and LSE in exact
+//    arithmetic; O is divided by the sum of the bf16-rounded terms that built the
+//    accumulator, so the weights applied to V sum to one whatever the reference.
 //  * Workgroup ids are remapped so that each XCD (8 per chip, dispatched
 //    round-robin) runs consecutive query tiles of the same head, keeping that
 //    head's K/V hot in the XCD's L2.
@@ -49,9 +53,6 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Rescale the accumulator only when a tile's max exceeds the reference by more
-// than this (log2 units); exp2 terms then stay <= 2^8, far from fp32/bf16 limits.
-constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
 struct Cfg {
@@ -293,24 +294,60 @@ struct Wave {
   unsigned gofs[C::kLoadsPerWave];  // this lane's tile_load_offset values
   f32x16_t acc[C::kDB][2];    // O^T accumulator (AGPRs)
   float m[2];                 // reference max, log2 units
-  float l[2];                 // this lane's part of the running sum
+  float l[2];                 // this lane's part of the running sum of the exp2 terms (for LSE)
+  float lb[2];                // ... of the same terms as rounded to bf16 for the PV product (for O)
   bf16x8_t vpre[4];           // V^T operands of the next step's first PV slots, read ahead
   bool rescale;               // the reference max moved in the last softmax: scale acc
   float alpha[2];             // ... by exp2(m_old - m_new) before the next PV product
 };
 
+// Online-softmax reference update for one 32-key sub-tile (FA1 page, derivation
+// steps 1-2), the slow path: the row max of the sub-tile, a new reference max
+// m_new = max(m, rowmax) per row, alpha = exp2(m_old - m_new), and l rescaled.
+// kMasked sets keys >= nvalid (passed as nvalid - 8g) to -inf first.
+template <bool kMasked>
+__device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], float (&l)[2], float (&lb)[2],
+                                               float (&alpha)[2], float c, int nv8) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float x = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (kMasked) {
+        if (key_of_reg(i) >= nv8) s[qb][i] = -__builtin_inff();
+      }
+      x = fmaxf(x, s[qb][i]);
+    }
+    const float mn = fmaxf(m[qb], pair_max(x) * c);
+    alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mn);
+    m[qb] = mn;
+    l[qb] *= alpha[qb];
+    lb[qb] *= alpha[qb];
+  }
+}
+
 // One pipeline step j over 32-key sub-tiles (FA1 page, derivation steps 1-5, with
 // the division by l deferred to the end). The matrix cores add sub-tile j-1's PV
 // product (kPV) and then compute the scores of sub-tile j+1 (kQK), while the VALU
-// does the online softmax of sub-tile j (kExp: steps 1-2 of the derivation,
-// scores in scur, exp2 terms into pcur), so no MFMA depends on a VALU result of
-// the same step. Issue order is fixed by sched_barrier fences: MFMA slot s is
-// followed by its share of the softmax work and by LDS reads issued ahead of use.
-// With kOneS the softmax finishes during the PV slots, so the scores of j+1 can
-// overwrite those of j (scur and snxt may be the same registers); otherwise it is
-// spread over all slots and scur/snxt must differ. kMasked: sub-tile j is the
-// ragged last one (keys >= nvalid, passed as nvalid - 8g, are masked).
-template <int D, bool kPV, bool kExp, bool kQK, bool kMasked, bool kOneS>
+// does the online softmax of sub-tile j (kExp: scores in scur, exp2 terms into
+// pcur), so no MFMA depends on a VALU result of the same step.
+//
+// Softmax: the exp2 terms are formed against the current reference max m without
+// computing the tile max first. If some row's sum of terms over the sub-tile
+// exceeds 2^16 (or is infinite: the first sub-tile, where m = -inf), the wave
+// takes a slow path that moves the reference to the row max (move_reference),
+// schedules the accumulator rescale for the next step and recomputes the terms.
+// Otherwise every term is at most 2^16, far inside fp32 and bf16 range, and in
+// exact arithmetic the result does not depend on the reference. In rounded
+// arithmetic the terms' bf16 rounding does; dividing O by the sum of the rounded
+// terms (lb) rather than of the exact ones cancels it for the terms that dominate
+// a row, whatever the reference. The work is staged over the PV slots:
+// slot s issues the fma of some registers, the exp2 of those of slot s-1 and the
+// sum and bf16 packing of those of slot s-2, so no instruction waits for one
+// issued in the same slot. The softmax runs through the score slots too, so scur
+// and snxt are different registers. kMasked: sub-tile j is the ragged last one (keys >=
+// nvalid, passed as nvalid - 8g, are masked).
+template <int D, bool kPV, bool kExp, bool kQK, bool kMasked>
 __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, const char* gk, const char* gv,
                                               LDS_AS char* lds, int wave, int lane, f32x16_t (&scur)[2],
                                               f32x16_t (&snxt)[2], const bf16x8_t (&pprev)[2][2],
@@ -319,12 +356,14 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   constexpr int KS = C::kKS, DB = C::kDB;
   constexpr int NPV = kPV ? 4 * DB : 0;        // MFMA slots of the PV product (first)
   constexpr int NS = NPV + (kQK ? 2 * KS : 0);  // all MFMA slots
-  constexpr int NI = kExp ? 5 + 32 : 0;        // softmax work items
-  constexpr int NVS = kOneS ? NPV : NS;        // slots that carry softmax work
+  constexpr int NE = 32;                       // score registers per lane (2 blocks x 16)
+  // Slots that issue fma work; exp2 and packing trail by one and two slots.
+  constexpr int NAS = NS >= 3 ? NS - 2 : 0;
   constexpr int NPAIR = 2 * DB;                // V^T operand pairs (h, db) of a PV product
   constexpr int kVPre = 4;                     // pairs read in the previous step
   constexpr int kVLead = 4;                    // other pairs: read this many pairs ahead
   constexpr int kKStart = NPV > 8 ? NPV - 8 : 0;  // slot where K operand reads start
+  constexpr float kSumLimit = 65536.0f;
   static_assert(NPAIR >= kVPre, "prefetch depth");
 
   if constexpr (kPV) {
@@ -342,6 +381,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
+      w.rescale = false;
     }
   }
   if constexpr (kQK) {
@@ -361,8 +401,8 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   __builtin_amdgcn_sched_barrier(0);
 
   // Byte offsets (uniform, SGPR) of this step's sub-tiles from the LDS base: K of
-  // j+1, V of j-1, and V of j (read ahead for the next step).
-  // readfirstlane: one scalar value each, so every operand address is one v_add.
+  // j+1, V of j-1, and V of j (read ahead for the next step). readfirstlane: one
+  // scalar value each, so every operand address is one v_add.
   const unsigned kst = __builtin_amdgcn_readfirstlane(
       kQK ? (unsigned)((((j + 1) >> 1) % C::kStages) * C::kStageBytes + ((j + 1) & 1) * 32 * C::kRowBytes) : 0u);
   const unsigned vst = __builtin_amdgcn_readfirstlane(
@@ -402,79 +442,92 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   // the VALU reads of it below.
   if constexpr (kExp) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(scur[0]), "+v"(scur[1]));
 
-  // Softmax state of this step.
-  float x[2] = {-__builtin_inff(), -__builtin_inff()};
-  float alpha[2] = {1.0f, 1.0f};
+  // ---- softmax of sub-tile j, staged: fma (A), exp2 (B), sum + pack (C) ----
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  float tv[2][16];
   float sum[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-  float peven[2];  // even-register exp2 term waiting for its odd partner
-  bool any = false;
-  auto valu_item = [&](auto it_tag) {
-    constexpr int it = decltype(it_tag)::value;
-    if constexpr (it < 4) {  // partial row max over 8 registers
-      constexpr int qb = it / 2, i0 = (it % 2) * 8;
-#pragma unroll
-      for (int i = i0; i < i0 + 8; ++i) {
-        if constexpr (kMasked) {
-          if (key_of_reg(i) >= nv8) scur[qb][i] = -__builtin_inff();
-        }
-        x[qb] = fmaxf(x[qb], scur[qb][i]);
-      }
-    } else if constexpr (it == 4) {  // tile max, reference update, l rescale
-      float mt[2];
-      bool need = false;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        mt[qb] = pair_max(x[qb]) * c;
-        need |= mt[qb] > w.m[qb] + kRescaleThreshold;
-      }
-      any = __builtin_amdgcn_ballot_w64(need) != 0;
-      // Branch-free: without a move, mt - inf = -inf leaves the reference as is.
-      const float off = any ? 0.0f : __builtin_inff();
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float mn = fmaxf(w.m[qb], mt[qb] - off);
-        alpha[qb] = __builtin_amdgcn_exp2f(w.m[qb] - mn);
-        w.m[qb] = mn;
-        w.l[qb] *= alpha[qb];
-      }
-    } else {  // one exp2 term: register i of block qb
-      constexpr int e = it - 5, qb = e / 16, i = e % 16;
-      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[qb][i], c, -w.m[qb]));
-      if constexpr (kMasked) {
-        if (key_of_reg(i) >= nv8) pv = 0.0f;
-      }
-      sum[qb][i & 1] += pv;
-      if constexpr ((i & 1) == 0) {
-        peven[qb] = pv;
-      } else {  // registers i-1, i -> one packed bf16 pair (v_cvt_pk_bf16_f32, nearest-even)
-        typedef float f32x2_t __attribute__((ext_vector_type(2)));
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-        const bf16x2_t pr = __builtin_convertvector((f32x2_t){peven[qb], pv}, bf16x2_t);
-        u32x4_t words = __builtin_bit_cast(u32x4_t, pcur[qb][i >> 3]);
-        words[(i & 7) >> 1] = __builtin_bit_cast(unsigned, pr);
-        pcur[qb][i >> 3] = __builtin_bit_cast(bf16x8_t, words);
+  float sumb[2] = {0.0f, 0.0f};
+  unsigned pk[2][8];  // packed bf16 pairs, assembled into pcur per 8-key operand
+  auto stage_a = [&](auto e_tag) {
+    constexpr int e = decltype(e_tag)::value, qb = e / 16, i = e % 16;
+    tv[qb][i] = __builtin_fmaf(scur[qb][i], c, -w.m[qb]);
+  };
+  auto stage_b = [&](auto e_tag) {
+    constexpr int e = decltype(e_tag)::value, qb = e / 16, i = e % 16;
+    float pe = __builtin_amdgcn_exp2f(tv[qb][i]);
+    if constexpr (kMasked) {
+      if (key_of_reg(i) >= nv8) pe = 0.0f;
+    }
+    tv[qb][i] = pe;
+  };
+  auto stage_c = [&](auto e_tag) {
+    constexpr int e = decltype(e_tag)::value, qb = e / 16, i = e % 16;
+    sum[qb][i & 1] += tv[qb][i];
+    if constexpr (i & 1) {  // registers i-1, i -> one packed bf16 pair (v_cvt_pk_bf16_f32, nearest-even)
+      const bf16x2_t pr = __builtin_convertvector((f32x2_t){tv[qb][i - 1], tv[qb][i]}, bf16x2_t);
+      // The rounded pair's sum, exact products with one (v_dot2c_f32_bf16).
+      sumb[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, (bf16x2_t){(__bf16)1.0f, (__bf16)1.0f}, sumb[qb], false);
+      pk[qb][i >> 1] = __builtin_bit_cast(unsigned, pr);
+      if constexpr ((i & 7) == 7) {  // a whole 8-key operand: assemble it once
+        constexpr int f = i >> 3;
+        pcur[qb][f] = __builtin_bit_cast(
+            bf16x8_t, (u32x4_t){pk[qb][4 * f], pk[qb][4 * f + 1], pk[qb][4 * f + 2], pk[qb][4 * f + 3]});
       }
     }
   };
+  // Elements whose fma is issued in slot s (s < NAS); exp2 in s+1, pack in s+2.
+  auto a_begin = [](int s) constexpr { return NAS > 0 ? (s * NE) / NAS : 0; };
+  auto softmax_slot = [&](auto s_tag) {
+    constexpr int s = decltype(s_tag)::value;
+    if constexpr (s < NAS) static_for<a_begin(s), a_begin(s + 1)>(stage_a);
+    if constexpr (s >= 1 && s - 1 < NAS) static_for<a_begin(s - 1), a_begin(s)>(stage_b);
+    if constexpr (s >= 2 && s - 2 < NAS) {
+      static_for<a_begin(s - 2), a_begin(s - 1)>(stage_c);
+      // Pin what this slot produced (packed words, rounded-term sums) to the slot,
+      // so later passes cannot sink the softmax past it. Single registers: pinning
+      // a partly built 4-register operand would make the compiler copy it.
+      auto& pkw = pk;  // named here: asm operands alone do not capture in a generic lambda
+      auto& sbw = sumb;
+#pragma unroll
+      for (int e = a_begin(s - 2) | 1; e < a_begin(s - 1); e += 2)
+        asm volatile("" : "+v"(pkw[e >> 4][(e & 15) >> 1]), "+v"(sbw[e >> 4]));
+    }
+  };
+  // After the last pack: the slow path if some row's terms grew too large.
   auto finish_softmax = [&]() {
     if constexpr (kExp) {
+      const bool big = (sum[0][0] + sum[0][1] > kSumLimit) || (sum[1][0] + sum[1][1] > kSumLimit);
+      if (__builtin_amdgcn_ballot_w64(big) != 0) {
+        float alpha[2];
+        move_reference<kMasked>(scur, w.m, w.l, w.lb, alpha, c, nv8);
+        w.alpha[0] = alpha[0];
+        w.alpha[1] = alpha[1];
+        w.rescale = kPV;  // before the first PV product acc is zero: nothing to rescale
+        sum[0][0] = sum[0][1] = sum[1][0] = sum[1][1] = 0.0f;
+        sumb[0] = sumb[1] = 0.0f;
+        static_for<0, NE>(stage_a);
+        static_for<0, NE>(stage_b);
+        static_for<0, NE>(stage_c);
+      }
       w.l[0] += sum[0][0] + sum[0][1];
       w.l[1] += sum[1][0] + sum[1][1];
-      // Before the first PV product acc is zero: nothing to rescale.
-      w.rescale = kPV && any;
-      w.alpha[0] = alpha[0];
-      w.alpha[1] = alpha[1];
+      w.lb[0] += sumb[0];
+      w.lb[1] += sumb[1];
     }
   };
+
   // Reads issued before the first slot.
   static_for<0, NPAIR>([&](auto p_tag) {
     constexpr int p = decltype(p_tag)::value;
     if constexpr (2 * (p - kVLead) < 0) load_v(p_tag);
   });
   if constexpr (kKStart == 0) static_for<0, 3>(load_k);
-  if constexpr (NVS == 0) {  // no slot carries softmax work: do it before any MFMA
-    static_for<0, NI>(valu_item);
+  if constexpr (kExp && NAS == 0) {  // too few slots to carry the softmax: do it before any MFMA
+    static_for<0, NE>(stage_a);
+    static_for<0, NE>(stage_b);
+    static_for<0, NE>(stage_c);
     finish_softmax();
   }
 
@@ -508,21 +561,10 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
         load_k(std::integral_constant<int, n + 3>{});
       }
     }
-    // This slot's share of the softmax work, pinned to the slot: the empty asm
-    // consumes the P operands produced so far, so later passes cannot sink the
-    // exp2 work past the slot.
-    if constexpr (s < NVS) {
-      constexpr int i0 = (s * NI) / NVS, i1 = ((s + 1) * NI) / NVS;
-      static_for<i0, i1>(valu_item);
-      if constexpr (i1 > 5) {
-        constexpr int e1 = i1 - 5;  // exp items done so far
-        if constexpr (e1 > 0) asm volatile("" : "+v"(pcur[0][0]));
-        if constexpr (e1 > 8) asm volatile("" : "+v"(pcur[0][1]));
-        if constexpr (e1 > 16) asm volatile("" : "+v"(pcur[1][0]));
-        if constexpr (e1 > 24) asm volatile("" : "+v"(pcur[1][1]));
-      }
+    if constexpr (kExp && NAS > 0) {
+      softmax_slot(s_tag);
+      if constexpr (s == NAS + 1) finish_softmax();
     }
-    if constexpr (s == NVS - 1) finish_softmax();
     __builtin_amdgcn_sched_barrier(0);
   });
   if constexpr (kExp && !kQK) {  // no score slots: read the next step's V operands now
@@ -599,6 +641,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   }
   w.m[0] = w.m[1] = -__builtin_inff();
   w.l[0] = w.l[1] = 0.0f;
+  w.lb[0] = w.lb[1] = 0.0f;
   w.rescale = false;
   w.alpha[0] = w.alpha[1] = 1.0f;
 #pragma unroll
@@ -635,13 +678,10 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(sa[0]), "+v"(sa[1]));
   }
 
-  // Step j: PV of j-1, softmax of j, scores of j+1. d = 128 keeps one score
-  // buffer (the softmax of j ends before the scores of j+1 are written); d = 64
-  // alternates two and spreads the softmax over every slot.
-  constexpr bool kOneS = D == 128;
-#define FA_STEP(PV, EXP, QK, MASK, J, SC, SN, PP, PC)                                                   \
-  pipeline_step<D, PV, EXP, QK, MASK, kOneS>(w, J, T, N, gk, gv, lds, wave, lane, (kOneS ? sa : SC), \
-                                             (kOneS ? sa : SN), PP, PC, c, nv8)
+  // Step j: PV of j-1, softmax of j, scores of j+1. Two score buffers alternate,
+  // so the softmax of j can spread over every MFMA slot of the step.
+#define FA_STEP(PV, EXP, QK, MASK, J, SC, SN, PP, PC) \
+  pipeline_step<D, PV, EXP, QK, MASK>(w, J, T, N, gk, gv, lds, wave, lane, SC, SN, PP, PC, c, nv8)
   if (U == 1) {
     if (ragged) FA_STEP(false, true, false, true, 0, sa, sb, pb, pa);
     else FA_STEP(false, true, false, false, 0, sa, sb, pb, pa);
@@ -675,13 +715,15 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   }
 #undef FA_STEP
 
-  // Epilogue: O = acc / l (bf16, nearest-even), LSE = ln2 * (m + log2 l).
+  // Epilogue: O = acc / lb (bf16, nearest-even), LSE = ln2 * (m + log2 l). O is
+  // divided by the sum of the bf16-rounded terms that formed acc, so the weights
+  // it applies to V sum to one exactly; LSE takes the sum of the unrounded terms.
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lsum = pair_sum(w.l[qb]);
-    const float inv = 1.0f / lsum;
+    const float inv = 1.0f / pair_sum(w.lb[qb]);
     const int row = q0 + qb * 32 + (lane & 31);
     if (row < N) {
       __bf16* dst = o + head_off + (size_t)row * D;

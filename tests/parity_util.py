@@ -16,11 +16,14 @@ LSE_TOL = 1e-3  # max |LSE_gpu - LSE_oracle|
 
 
 def bf16_half_ulp(x):
-    """Half a bf16 ulp at |x|: the error that rounding the exact O to the bf16 output
-    alone can carry. bf16 keeps 8 significant bits, so for |x| in [2^e, 2^(e+1)) the
-    ulp is 2^(e-7). For |x| >= 4 this exceeds 1e-2 by itself, which is why the
-    absolute O tolerance is applied on top of it (the comparison with the unfused
-    yardstick, which carries the same rounding, stays as stated)."""
+    """Half a bf16 ulp at |x|: the error that rounding a value of that size to the
+    bf16 output carries by itself. bf16 keeps 8 significant bits, so for |x| in
+    [2^e, 2^(e+1)) the ulp is 2^(e-7). For |x| >= 4 this exceeds 1e-2 by itself,
+    which is why the absolute O tolerance is applied on top of it (the comparison
+    with the unfused yardstick, which carries the same rounding, stays as stated).
+    The rounding happens at the computed value's size, which can sit just above a
+    power of two while the exact value sits just below it, so callers evaluate it
+    at the larger of the two magnitudes."""
     ax = np.maximum(np.abs(x), 2.0 ** -126)
     return 2.0 ** (np.floor(np.log2(ax)) - 8)
 
@@ -49,7 +52,8 @@ def gpu_errors(q, k, v, o_gpu, lse_gpu, scale, rows=None, with_unfused=True):
     dO = np.abs(o - O_ref)
     out = {
         "max_dO": float(dO.max()) if o.size else 0.0,
-        "max_dO_beyond_rounding": float((dO - bf16_half_ulp(O_ref)).max()) if o.size else 0.0,
+        "max_dO_beyond_rounding": float((dO - bf16_half_ulp(np.maximum(np.abs(O_ref), np.abs(o)))).max())
+        if o.size else 0.0,
         "max_dLSE": float(np.abs(lse - L_ref).max()) if lse.size else 0.0,
         "finite": bool(np.isfinite(o).all() and np.isfinite(lse).all()),
     }
