@@ -30,10 +30,11 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz (A
 HBM_PEAK_GBS = 8000.0
 METRIC = "fwd attention TFLOP/s & % of bf16 MFMA peak, B=1 H=32 N=8192 d=128"
 KERNEL_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_fwd.hip")
+UNFUSED_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_unfused.hip")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -93,9 +94,13 @@ def _read_counter_csv(path):
     return {k: [v for _, v in sorted(vals)] for k, vals in out.items()}
 
 
-def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes):
-    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel by what the
-    same counters read for the plain copy of ``copy_bytes`` bytes in the same run."""
+UNFUSED_KERNELS = ("unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel")
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel (or of the
+    three unfused kernels, summed per launch) by what the same counters read for the
+    plain copy of ``copy_bytes`` bytes in the same run."""
     import attn_inputs
 
     w = attn_inputs.HEADLINE if workload is None else attn_inputs.WORKLOAD_BY_NAME[workload]
@@ -108,19 +113,30 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes):
             raise SystemExit(f"no {counter} values for the requested kernel in the CSV")
         return vals
 
-    is_fa = lambda k: "fa_fwd_kernel" in k
+    def per_launch(table, counter):
+        """Average KiB per launch: one kernel (fused) or the sum of the three."""
+        names = UNFUSED_KERNELS if unfused else ("fa_fwd_kernel",)
+        total, raw = 0.0, []
+        for name in names:
+            vals = pick(table, counter, lambda k, n=name: n in k)
+            total += sum(vals) / len(vals)
+            raw.append(vals)
+        per = [round(sum(r[i] for r in raw), 1) for i in range(min(len(r) for r in raw))]
+        return total, per
+
     is_copy = lambda k: "fa_fwd_kernel" not in k and "unf_" not in k
     copy_fetch = pick(fetch, "FETCH_SIZE", is_copy)[0] * 1024.0
     copy_write = pick(write, "WRITE_SIZE", is_copy)[0] * 1024.0
     f_scale = copy_bytes / copy_fetch
     w_scale = copy_bytes / copy_write
-    fa_fetch = pick(fetch, "FETCH_SIZE", is_fa)
-    fa_write = pick(write, "WRITE_SIZE", is_fa)
-    fetch_b = sum(fa_fetch) / len(fa_fetch) * 1024.0 * f_scale
-    write_b = sum(fa_write) / len(fa_write) * 1024.0 * w_scale
+    fa_fetch_kib, fa_fetch = per_launch(fetch, "FETCH_SIZE")
+    fa_write_kib, fa_write = per_launch(write, "WRITE_SIZE")
+    fetch_b = fa_fetch_kib * 1024.0 * f_scale
+    write_b = fa_write_kib * 1024.0 * w_scale
     rec = {
         "workload": w.name,
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "path": "unfused-3-kernel" if unfused else "fused",
+        "kernel_source_sha256_16": kernel_source_hash(UNFUSED_SRC if unfused else KERNEL_SRC),
         "hbm_bytes_per_launch": round(fetch_b + write_b),
         "fetch_bytes_per_launch": round(fetch_b),
         "write_bytes_per_launch": round(write_b),
@@ -129,13 +145,49 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes):
         "copy_calibration_bytes": copy_bytes,
         "fetch_scale": round(f_scale, 4),
         "write_scale": round(w_scale, 4),
-        "fetch_kib_raw_per_launch": [round(v, 1) for v in fa_fetch],
-        "write_kib_raw_per_launch": [round(v, 1) for v in fa_write],
+        "fetch_kib_raw_per_launch": fa_fetch,
+        "write_kib_raw_per_launch": fa_write,
     }
-    path = os.path.join(ROOT, "profiles", f"fa_fwd_{w.name}_traffic.json")
+    stem = "fa_unfused" if unfused else "fa_fwd"
+    path = os.path.join(ROOT, "profiles", f"{stem}_{w.name}_traffic.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def summarize_trace(stats_csv, command, workload):
+    """Write the per-kernel duration summary of a rocprofv3 --stats run, with the
+    command that produced it and the algorithmic rate at the average duration."""
+    import csv
+
+    import attn_inputs
+
+    w = attn_inputs.HEADLINE if workload is None else attn_inputs.WORKLOAD_BY_NAME[workload]
+    rows = list(csv.DictReader(open(stats_csv)))
+    fused = any("fa_fwd_kernel" in r["Name"] for r in rows)
+    lines = [f"# Kernel durations, workload {w.name} (B={w.B} H={w.H} N={w.N} d={w.d})", "",
+             "Command, run from the repository root with TMPDIR=/tmp:", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | stddev us |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        short = name[:60]
+        for base in ("fa_fwd_kernel", "unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel"):
+            if base in name:
+                dim = next((dd for dd in ("128", "64") if f"<{dd}>" in name or f"ILi{dd}E" in name), None)
+                short = f"{base}<{dim}>" if dim else base
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['StdDev']) / 1e3:.1f} |")
+    if fused:
+        r = next(r for r in rows if "fa_fwd_kernel" in r["Name"])
+        avg_s = float(r["AverageNs"]) * 1e-9
+        tf = w.flops / avg_s / 1e12
+        lines += ["", f"Fused kernel at its average duration: {w.flops:.4e} FLOP per launch -> {tf:.1f} TFLOP/s, "
+                      f"{tf / MFMA_BF16_PEAK_TFLOPS:.4f} of the {MFMA_BF16_PEAK_TFLOPS} TFLOP/s bf16 MFMA peak.",
+                  f"Kernel source sha256[:16] of fa_fwd.hip: {kernel_source_hash()}."]
+    path = os.path.join(ROOT, "profiles", f"{'fa_fwd' if fused else 'fa_unfused'}_{w.name}_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -154,10 +206,17 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: read two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-calibration run and write profiles/fa_fwd_<workload>_traffic.json")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"),
+                    help="no GPU work: turn a rocprofv3 --kernel-trace --stats kernel_stats.csv into "
+                         "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin")
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_calibration)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_calibration,
+                      unfused=args.unfused)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
