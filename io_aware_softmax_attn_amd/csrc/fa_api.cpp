@@ -12,9 +12,11 @@ namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 
+// Whether [a, a+na) and [b, b+nb) share a byte. Written with differences only, so
+// ranges near the top of the address space cannot wrap the comparison.
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
-  return pa < pb + nb && pb < pa + na;
+  return pa <= pb ? pb - pa < na : pa - pb < nb;
 }
 
 bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {

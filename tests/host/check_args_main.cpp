@@ -1,0 +1,140 @@
+// Host-only test of the C ABI's validation and dispatch layer (fa_api.cpp,
+// fa_select.cpp), built with g++ under AddressSanitizer and UBSan. The HIP side
+// is replaced by the stubs below: they count launches, so every rejected call can
+// be shown to return before anything would be enqueued.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+
+#include "../../include/fa.h"
+#include "../../io_aware_softmax_attn_amd/csrc/fa_internal.h"
+
+namespace {
+int g_launches = 0;
+int g_device = 1;  // what device_is_gfx950 reports
+int g_failures = 0;
+
+void expect(bool ok, const char* what, int line) {
+  if (!ok) {
+    std::printf("FAIL line %d: %s\n", line, what);
+    ++g_failures;
+  }
+}
+#define EXPECT(c) expect((c), #c, __LINE__)
+}  // namespace
+
+namespace fa {
+int launch_fused(const void*, const void*, const void*, void*, float*, int, int, int, int, float, const Blocks&,
+                 void*) {
+  ++g_launches;
+  return FA_OK;
+}
+int launch_unfused(const void*, const void*, const void*, void*, float*, int, int, int, int, float, void*, void*) {
+  ++g_launches;
+  return FA_OK;
+}
+int device_is_gfx950() { return g_device; }
+}  // namespace fa
+
+int main() {
+  // Real, aligned host buffers for a B=2 H=3 N=100 d=64 problem (never dereferenced
+  // by the library; ASan would report it if they were read out of bounds).
+  const int B = 2, H = 3, N = 100, d = 64;
+  const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
+  char* q = static_cast<char*>(std::aligned_alloc(256, tb));
+  char* k = static_cast<char*>(std::aligned_alloc(256, tb));
+  char* v = static_cast<char*>(std::aligned_alloc(256, tb));
+  char* o = static_cast<char*>(std::aligned_alloc(256, tb));
+  float* lse = static_cast<float*>(std::aligned_alloc(256, (lb + 255) / 256 * 256));
+  const float sc = 0.125f;
+
+  // Valid call: one launch; with a non-gfx950 device: an error and none.
+  EXPECT(fa_check_args(q, k, v, o, lse, B, H, N, d, sc, 0, nullptr, 0) == FA_OK);
+  EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, sc, nullptr) == FA_OK && g_launches == 1);
+  g_device = 0;
+  EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, sc, nullptr) == FA_ERR_DEVICE && g_launches == 1);
+  g_device = FA_ERR_HIP;
+  EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, sc, nullptr) == FA_ERR_HIP && g_launches == 1);
+  g_device = 1;
+
+  // Every argument error returns its code and launches nothing.
+  const int before = g_launches;
+  EXPECT(fa_fwd(nullptr, k, v, o, lse, B, H, N, d, sc, nullptr) == FA_ERR_NULL);
+  EXPECT(fa_fwd(q, k, v, o, nullptr, B, H, N, d, sc, nullptr) == FA_ERR_NULL);
+  EXPECT(fa_fwd(q, k, v, o, lse, -1, H, N, d, sc, nullptr) == FA_ERR_SHAPE);
+  EXPECT(fa_fwd(q, k, v, o, lse, B, H, -5, d, sc, nullptr) == FA_ERR_SHAPE);
+  EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, 96, sc, nullptr) == FA_ERR_HEADDIM);
+  EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, 0, sc, nullptr) == FA_ERR_HEADDIM);
+  EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, std::nanf(""), nullptr) == FA_ERR_SCALE);
+  EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, INFINITY, nullptr) == FA_ERR_SCALE);
+  EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, -0.5f, nullptr) == FA_ERR_SCALE);
+  EXPECT(fa_fwd(q + 8, k, v, o, lse, B, H, N, d, sc, nullptr) == FA_ERR_ALIGN);
+  EXPECT(fa_fwd(q, k, v, o + 2, lse, B, H, N, d, sc, nullptr) == FA_ERR_ALIGN);
+  EXPECT(fa_fwd(q, k, v, o, reinterpret_cast<float*>(reinterpret_cast<char*>(lse) + 2), B, H, N, d, sc, nullptr) ==
+         FA_ERR_ALIGN);
+  EXPECT(fa_fwd(q, k, v, q, lse, B, H, N, d, sc, nullptr) == FA_ERR_ALIAS);             // o is q
+  EXPECT(fa_fwd(q, k, v, k + 1024, lse, B, H, N, d, sc, nullptr) == FA_ERR_ALIAS);      // o inside k
+  EXPECT(fa_fwd(q, k, v, o, reinterpret_cast<float*>(o + 64), B, H, N, d, sc, nullptr) == FA_ERR_ALIAS);
+  EXPECT(fa_fwd(q, k, v, o, reinterpret_cast<float*>(v), B, H, N, d, sc, nullptr) == FA_ERR_ALIAS);
+  EXPECT(fa_fwd(q, k, v, o, lse, 65536, 65536, 65536, d, sc, nullptr) == FA_ERR_OVERFLOW);
+  const int imax = std::numeric_limits<int>::max();
+  EXPECT(fa_fwd(q, k, v, o, lse, imax, imax, imax, 128, sc, nullptr) == FA_ERR_OVERFLOW);
+  EXPECT(fa_fwd(q, k, v, o, lse, 1, 1 << 16, 1 << 24, 128, sc, nullptr) == FA_ERR_OVERFLOW);  // grid > 2^31
+  EXPECT(g_launches == before);
+
+  // Q, K and V may share memory; an empty problem is a no-op even with null pointers.
+  EXPECT(fa_check_args(q, q, q, o, lse, B, H, N, d, sc, 0, nullptr, 0) == FA_OK);
+  EXPECT(fa_fwd(nullptr, nullptr, nullptr, nullptr, nullptr, 0, H, N, d, sc, nullptr) == FA_OK);
+  EXPECT(fa_fwd(nullptr, nullptr, nullptr, nullptr, nullptr, B, H, 0, d, sc, nullptr) == FA_OK);
+  EXPECT(g_launches == before);
+  // scale = 0 is allowed (the uniform average).
+  EXPECT(fa_check_args(q, k, v, o, lse, B, H, N, d, 0.0f, 0, nullptr, 0) == FA_OK);
+
+  // Overlap arithmetic at the top of the address space: adjacent ranges that end at
+  // the last byte do not overlap; ranges that share it do.
+  const uintptr_t top = std::numeric_limits<uintptr_t>::max() - tb + 1;  // o ends at the last byte
+  const void* o_top = reinterpret_cast<const void*>(top & ~uintptr_t(255));
+  EXPECT(fa_check_args(q, k, v, o_top, lse, B, H, N, d, sc, 0, nullptr, 0) == FA_OK);
+  const void* q_top = reinterpret_cast<const void*>((top & ~uintptr_t(255)) + 256);
+  EXPECT(fa_check_args(q_top, k, v, o_top, lse, B, H, N, d, sc, 0, nullptr, 0) == FA_ERR_ALIAS);
+
+  // Unfused: workspace size, and each workspace error.
+  const size_t need = fa_unfused_workspace_bytes(B, H, N);
+  EXPECT(need == (size_t)6 * B * H * N * 128);  // N = 100 padded to 128 columns; already a multiple of 256
+  EXPECT(fa_unfused_workspace_bytes(1, 1, 1) == 512);  // 6 * 64 = 384, rounded up to 256
+  EXPECT(fa_unfused_workspace_bytes(0, 5, 5) == 0);
+  EXPECT(fa_unfused_workspace_bytes(-1, 5, 5) == 0);
+  EXPECT(fa_unfused_workspace_bytes(imax, imax, imax) == 0);
+  char* ws = static_cast<char*>(std::aligned_alloc(256, need + 256));
+  EXPECT(fa_unfused_fwd(q, k, v, o, lse, B, H, N, d, sc, ws, need, nullptr) == FA_OK && g_launches == before + 1);
+  EXPECT(fa_unfused_fwd(q, k, v, o, lse, B, H, N, d, sc, nullptr, need, nullptr) == FA_ERR_WORKSPACE);
+  EXPECT(fa_unfused_fwd(q, k, v, o, lse, B, H, N, d, sc, ws, need - 1, nullptr) == FA_ERR_WORKSPACE);
+  EXPECT(fa_unfused_fwd(q, k, v, o, lse, B, H, N, d, sc, ws + 8, need, nullptr) == FA_ERR_WORKSPACE);
+  EXPECT(fa_unfused_fwd(q, k, v, o, lse, B, H, N, d, sc, q, need, nullptr) == FA_ERR_WORKSPACE);
+  EXPECT(g_launches == before + 1);
+
+  // Selector and strings.
+  int br = 0, bc = 0, nw = 0;
+  EXPECT(fa_select_blocks(128, 8192, 1, 32, &br, &bc, &nw) == FA_OK && br == 256 && bc == 64 && nw == 4);
+  EXPECT(fa_select_blocks(64, 1024, 4, 16, &br, &bc, &nw) == FA_OK && br == 256 && bc == 64 && nw == 4);
+  EXPECT(fa_select_blocks(80, 1024, 4, 16, &br, &bc, &nw) == FA_ERR_HEADDIM);
+  EXPECT(fa_select_blocks(64, 1024, 4, 16, nullptr, &bc, &nw) == FA_ERR_NULL);
+  for (int s = FA_ERR_DEVICE; s <= FA_OK; ++s) {
+    const char* str = fa_status_string(s);
+    EXPECT(str != nullptr && std::strlen(str) > 0 && std::strcmp(str, "unknown status") != 0);
+  }
+  EXPECT(std::strcmp(fa_status_string(12345), "unknown status") == 0);
+  EXPECT(fa_version() >= 10000);
+
+  std::free(ws);
+  std::free(q);
+  std::free(k);
+  std::free(v);
+  std::free(o);
+  std::free(lse);
+  if (g_failures == 0) std::printf("check_args: all passed\n");
+  return g_failures == 0 ? 0 : 1;
+}
