@@ -131,10 +131,8 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // compiler from moving LDS accesses across the barrier.
 template <int kOutstanding>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(kOutstanding == 0 || kOutstanding == 4 || kOutstanding == 8, "add the count");
-  if constexpr (kOutstanding == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (kOutstanding == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  if constexpr (kOutstanding == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  static_assert(kOutstanding >= 0 && kOutstanding <= 63, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOutstanding) : "memory");
 }
 
 // kOutstanding: this wave's loads of later tiles that may stay in flight (loads
@@ -161,55 +159,53 @@ __device__ __forceinline__ unsigned tile_load_offset(int wave, int lane, int i, 
   return (unsigned)(row * (D * 2) + chunk * 16);
 }
 
-// One 16-byte-per-lane direct global->LDS load (global_load_lds_dwordx4): lane l's
-// 16 bytes land at LDS address lds_addr + 16*l. Issued through asm so that the
-// compiler, which cannot tell that the destination stage is disjoint from the
-// stages being read, does not put a vmcnt(0) wait in front of the next LDS read;
-// the pipeline waits for these loads itself (tile_barrier). M0 carries the LDS
-// address (one wait state between its write and the load).
-__device__ __forceinline__ void dma16(const char* gbase, unsigned voff, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(gbase)
-               : "memory", "m0");
+// Buffer resource over the part of K or V tile u of one head (head = that head's
+// base) that lies inside N: at most one tile, none for tiles past the end. A
+// buffer load outside it returns zeros without touching memory, so the ragged
+// last tile and the loads issued past the last tile need no clamping and no
+// branch. Word 3 selects raw 32-bit data (no swizzle, no index stride).
+// Words: base address bits 0-31, bits 32-47 (stride 0), size in bytes, format.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+constexpr unsigned kRawBufferWord3 = 0x00020000u;
+template <int D>
+__device__ __forceinline__ u32x4_t tile_rsrc(const char* head, int u, int N) {
+  using C = Cfg<D>;
+  const int rows = min(max(N - u * C::kBC, 0), C::kBC);
+  const uint64_t base = (uint64_t)(uintptr_t)head + (uint64_t)u * C::kTileBytes;
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)base);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(base >> 32) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane((unsigned)(rows * C::kRowBytes));
+  r[3] = kRawBufferWord3;
+  return r;
 }
-__device__ __forceinline__ void dma16_abs(const char* gaddr, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+
+// One 16-byte-per-lane direct global->LDS load (buffer_load_dwordx4 ... lds):
+// lane l's 16 bytes, at byte offset voff of the resource, land at LDS address
+// lds_addr + 16*l. Issued through asm so that the compiler, which cannot tell that
+// the destination stage is disjoint from the stages being read, does not put a
+// vmcnt(0) wait in front of the next LDS read; the pipeline waits for these loads
+// itself (tile_barrier). M0 carries the LDS address (one wait state between its
+// write and the load).
+__device__ __forceinline__ void dma16(u32x4_t rsrc, unsigned voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(lds_addr), "v"(gaddr)
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
 
-// Issue the direct-to-LDS loads of K and V tile t of one head into `stage`.
-// gofs holds this lane's tile_load_offset values. In the last, partial tile rows
-// past N re-read row N-1: finite data whose scores are masked to -inf.
-template <int D>
-__device__ __forceinline__ void issue_tile(const char* __restrict__ gk, const char* __restrict__ gv, int t, int N,
-                                           LDS_AS char* stage, int wave, int lane, const unsigned* gofs) {
+// Issue this wave's loads of K tile u (kV = false) or V tile u (kV = true) of one
+// head into `stage`, loads i0 .. i1-1. gofs holds this lane's tile_load_offset values.
+template <int D, bool kV>
+__device__ __forceinline__ void issue_half(const char* __restrict__ head, int u, int N, unsigned stage, int wave,
+                                           const unsigned* gofs, int i0, int i1) {
   using C = Cfg<D>;
-  const size_t tb = (size_t)t * C::kBC * (D * 2);
-  const unsigned sbase = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)stage);
-  if ((t + 1) * C::kBC <= N) {
-    const char* tk = gk + tb;
-    const char* tv = gv + tb;
+  const u32x4_t r = tile_rsrc<D>(head, u, N);
+  const unsigned dst = __builtin_amdgcn_readfirstlane(stage + (kV ? C::kTileBytes : 0) +
+                                                      (unsigned)(wave * C::kLoadsPerWave * 1024));
 #pragma unroll
-    for (int i = 0; i < C::kLoadsPerWave; ++i) {
-      const unsigned dst = sbase + (unsigned)((wave * C::kLoadsPerWave + i) * 1024);
-      dma16(tk, gofs[i], dst);
-      dma16(tv, gofs[i], dst + C::kTileBytes);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < C::kLoadsPerWave; ++i) {
-      const unsigned dst = sbase + (unsigned)((wave * C::kLoadsPerWave + i) * 1024);
-      int row;
-      const unsigned off = tile_load_offset<D>(wave, lane, i, &row);
-      const int grow = min(t * C::kBC + row, N - 1);
-      const size_t goff = (size_t)grow * (D * 2) + (off - (unsigned)row * (D * 2));
-      dma16_abs(gk + goff, dst);
-      dma16_abs(gv + goff, dst + C::kTileBytes);
-    }
-  }
+  for (int i = 0; i < C::kLoadsPerWave; ++i)
+    if (i >= i0 && i < i1) dma16(r, gofs[i], dst + i * 1024);
 }
 
 // ---------------------------------------------------------------------------
@@ -385,19 +381,32 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     }
   }
   if constexpr (kQK) {
-    if (j & 1) {  // sub-tile j+1 opens K/V tile t: wait for it, then start loading tile t+kAhead
-      static_assert(C::kAhead == 2, "the wait below assumes one later tile in flight");
+    if (j & 1) {  // sub-tile j+1 opens K/V tile t: wait for it
+      static_assert(C::kAhead >= 1 && C::kAhead <= 3, "wait counts below cover up to two later tiles");
+      constexpr int kPerTile = 2 * C::kLoadsPerWave;  // this wave's loads per K/V tile
       const int t = (j + 1) >> 1;
-      if (t + 1 < T) {
-        tile_barrier<2 * C::kLoadsPerWave>();
+      // Tiles t+1 .. t+kAhead-1 (those that exist) may stay in flight.
+      const int later = min(C::kAhead - 1, T - 1 - t);
+      if (later >= 2) {
+        tile_barrier<2 * kPerTile>();
+      } else if (later == 1) {
+        tile_barrier<kPerTile>();
       } else {
         tile_barrier<0>();
       }
-      if (t + C::kAhead < T)
-        issue_tile<D>(gk, gv, t + C::kAhead, N, lds + ((t + C::kAhead) % C::kStages) * C::kStageBytes, wave, lane,
-                      w.gofs);
     }
   }
+  // Loads of K/V tile u = t + kAhead, spread over the MFMA slots of the two steps of
+  // tile t: the step that opens it (j odd) loads u's K tile, the next one its V tile.
+  // Stage u % kStages last held tile u - kStages = t - 2, whose final operand reads
+  // completed in step 2t - 2, before the barrier above.
+  // Past the last tile the resource is empty and the loads only zero a free stage.
+  const int u_dma = ((j + 1) >> 1) + C::kAhead;
+  const bool dma_v = ((j + 1) & 1) != 0;
+  const u32x4_t dma_rsrc = tile_rsrc<D>(dma_v ? gv : gk, u_dma, N);
+  const unsigned dma_dst = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)lds + (unsigned)((u_dma % C::kStages) * C::kStageBytes + (dma_v ? C::kTileBytes : 0) +
+                                           wave * C::kLoadsPerWave * 1024));
   __builtin_amdgcn_sched_barrier(0);
 
   // Byte offsets (uniform, SGPR) of this step's sub-tiles from the LDS base: K of
@@ -445,7 +454,6 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   // ---- softmax of sub-tile j, staged: fma (A), exp2 (B), sum + pack (C) ----
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   float tv[2][16];
   float sum[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
   float sumb[2] = {0.0f, 0.0f};
@@ -561,6 +569,13 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
         load_k(std::integral_constant<int, n + 3>{});
       }
     }
+    if constexpr (kQK) {
+      constexpr int L = C::kLoadsPerWave, every = NS / L;
+      if constexpr (s % every == 1 && s / every < L) {
+        constexpr int i = s / every;
+        dma16(dma_rsrc, w.gofs[i], dma_dst + i * 1024);
+      }
+    }
     if constexpr (kExp && NAS > 0) {
       softmax_slot(s_tag);
       if constexpr (s == NAS + 1) finish_softmax();
@@ -604,7 +619,9 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
     w.gofs[i] = tile_load_offset<D>(wave, lane, i, &row);
   }
   // Start streaming K/V tile 0 while Q is loaded.
-  issue_tile<D>(gk, gv, 0, N, lds, wave, lane, w.gofs);
+  const unsigned lds_u = (unsigned)(uintptr_t)lds;
+  issue_half<D, false>(gk, 0, N, lds_u, wave, w.gofs, 0, C::kLoadsPerWave);
+  issue_half<D, true>(gv, 0, N, lds_u, wave, w.gofs, 0, C::kLoadsPerWave);
 
   // Q^T operand fragments: lane holds query q0 + qb*32 + lane%32, d = ks*16 + g*8 .. +8.
 #pragma unroll
@@ -652,9 +669,15 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
 
   wait_vmem();
   __syncthreads();
+  // Tiles 1 .. kAhead-1 and the K half of tile kAhead; from step 0 on each step
+  // loads one half of a later tile.
 #pragma unroll
-  for (int t = 1; t <= C::kAhead; ++t)
-    if (t < T) issue_tile<D>(gk, gv, t, N, lds + t * C::kStageBytes, wave, lane, w.gofs);
+  for (int t = 1; t <= C::kAhead; ++t) {
+    if (t < T) {
+      issue_half<D, false>(gk, t, N, lds_u + t * C::kStageBytes, wave, w.gofs, 0, C::kLoadsPerWave);
+      if (t < C::kAhead) issue_half<D, true>(gv, t, N, lds_u + t * C::kStageBytes, wave, w.gofs, 0, C::kLoadsPerWave);
+    }
+  }
 
   const int nvalid_last = N - (U - 1) * 32;  // 1..32 keys in the last sub-tile
   const bool ragged = nvalid_last < 32;
@@ -714,6 +737,10 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
     FA_STEP(true, false, false, false, 1, sb, sa, pa, pb);
   }
 #undef FA_STEP
+
+  // Loads issued after the last tile barrier (zero fills past the last tile) must
+  // land before the workgroup's LDS can be handed to another workgroup.
+  wait_vmem();
 
   // Epilogue: O = acc / lb (bf16, nearest-even), LSE = ln2 * (m + log2 l). O is
   // divided by the sum of the bf16-rounded terms that formed acc, so the weights
