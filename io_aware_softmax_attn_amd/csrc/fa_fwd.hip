@@ -226,6 +226,22 @@ __device__ __forceinline__ void mfma_s0(f32x16_t& d, const bf16x8_t& a, const bf
 __device__ __forceinline__ void mfma_o(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
+// Row sums of a P^T operand: v_mfma_f32_16x16x32_bf16 with a 0/1 selector as A.
+// Read as the B operand of this instruction, lane l of a P^T fragment holds 8 of
+// the 32 k-values of column l%16: k-group l/16, which is keys 0-7 of query l%32
+// for lanes 0-31 and keys 8-15 of query l%32 for lanes 32-63. The selector makes
+// output rows 0-7 sum k-groups 0 and 2 (query n) and rows 8-15 k-groups 1 and 3
+// (query n+16), so lane l of the result holds the full 16-key sum of query
+// (l%16) + 16*(l/32), in all four of its registers. Products with 0 and 1 are
+// exact and the sum is fp32, so this is the sum of the bf16 terms the PV product
+// used. The selector is tied as read-write so the compiler keeps it in place
+// instead of rewriting it (with a VALU move) in front of every use; the s_nop
+// covers the two wait states a VALU write needs before an MFMA reads it, should
+// the compiler ever move it anyway.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void mfma_rowsum(f32x4_t& d, bf16x8_t& sel, const bf16x8_t& p) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d), "+v"(sel) : "v"(p));
+}
 
 // Wait states between the last MFMA that wrote an accumulator and VALU reads of it.
 __device__ __forceinline__ void sync_acc(f32x16_t& a, f32x16_t& b) {
@@ -291,7 +307,8 @@ struct Wave {
   f32x16_t acc[C::kDB][2];    // O^T accumulator (AGPRs)
   float m[2];                 // reference max, log2 units
   float l[2];                 // this lane's part of the running sum of the exp2 terms (for LSE)
-  float lb[2];                // ... of the same terms as rounded to bf16 for the PV product (for O)
+  f32x4_t lbacc[2];           // row sums of the bf16 terms that entered the PV product (for O)
+  bf16x8_t sel;               // the 0/1 selector operand of mfma_rowsum
   bf16x8_t vpre[4];           // V^T operands of the next step's first PV slots, read ahead
   bool rescale;               // the reference max moved in the last softmax: scale acc
   float alpha[2];             // ... by exp2(m_old - m_new) before the next PV product
@@ -302,8 +319,8 @@ struct Wave {
 // m_new = max(m, rowmax) per row, alpha = exp2(m_old - m_new), and l rescaled.
 // kMasked sets keys >= nvalid (passed as nvalid - 8g) to -inf first.
 template <bool kMasked>
-__device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], float (&l)[2], float (&lb)[2],
-                                               float (&alpha)[2], float c, int nv8) {
+__device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], float (&l)[2], float (&alpha)[2],
+                                               float c, int nv8) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float x = -__builtin_inff();
@@ -318,7 +335,6 @@ __device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], 
     alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mn);
     m[qb] = mn;
     l[qb] *= alpha[qb];
-    lb[qb] *= alpha[qb];
   }
 }
 
@@ -375,6 +391,15 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
         w.acc[f >> 1][f & 1] *= w.alpha[f & 1];
         if (f + 1 < 2 * DB) asm volatile("" : "+a"(w.acc[f >> 1][f & 1]), "+a"(w.acc[(f + 1) >> 1][(f + 1) & 1]));
       }
+      // The row-sum MFMAs of the previous step finished during sync_acc's wait; the
+      // empty asm keeps the reads below after it. Lane l's row sum belongs to query
+      // (l%16) + 16*(l/32) (see mfma_rowsum), whose alpha sits in lane (that query).
+      asm volatile("" : "+v"(w.lbacc[0]), "+v"(w.lbacc[1]));
+      const int src = ((lane & 15) | ((lane >> 5) << 4)) * 4;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        w.lbacc[qb] *= __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, w.alpha[qb])));
+      asm volatile("s_nop 1" : "+v"(w.lbacc[0]), "+v"(w.lbacc[1]));
 #pragma unroll
       for (int db = 0; db < DB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
       w.rescale = false;
@@ -456,7 +481,6 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   float tv[2][16];
   float sum[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-  float sumb[2] = {0.0f, 0.0f};
   unsigned pk[2][8];  // packed bf16 pairs, assembled into pcur per 8-key operand
   auto stage_a = [&](auto e_tag) {
     constexpr int e = decltype(e_tag)::value, qb = e / 16, i = e % 16;
@@ -475,8 +499,6 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     sum[qb][i & 1] += tv[qb][i];
     if constexpr (i & 1) {  // registers i-1, i -> one packed bf16 pair (v_cvt_pk_bf16_f32, nearest-even)
       const bf16x2_t pr = __builtin_convertvector((f32x2_t){tv[qb][i - 1], tv[qb][i]}, bf16x2_t);
-      // The rounded pair's sum, exact products with one (v_dot2c_f32_bf16).
-      sumb[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, (bf16x2_t){(__bf16)1.0f, (__bf16)1.0f}, sumb[qb], false);
       pk[qb][i >> 1] = __builtin_bit_cast(unsigned, pr);
       if constexpr ((i & 7) == 7) {  // a whole 8-key operand: assemble it once
         constexpr int f = i >> 3;
@@ -493,14 +515,12 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     if constexpr (s >= 1 && s - 1 < NAS) static_for<a_begin(s - 1), a_begin(s)>(stage_b);
     if constexpr (s >= 2 && s - 2 < NAS) {
       static_for<a_begin(s - 2), a_begin(s - 1)>(stage_c);
-      // Pin what this slot produced (packed words, rounded-term sums) to the slot,
-      // so later passes cannot sink the softmax past it. Single registers: pinning
-      // a partly built 4-register operand would make the compiler copy it.
+      // Pin the packed words this slot produced to the slot, so later passes cannot
+      // sink the softmax past it. Single registers: pinning a partly built
+      // 4-register operand would make the compiler copy it.
       auto& pkw = pk;  // named here: asm operands alone do not capture in a generic lambda
-      auto& sbw = sumb;
 #pragma unroll
-      for (int e = a_begin(s - 2) | 1; e < a_begin(s - 1); e += 2)
-        asm volatile("" : "+v"(pkw[e >> 4][(e & 15) >> 1]), "+v"(sbw[e >> 4]));
+      for (int e = a_begin(s - 2) | 1; e < a_begin(s - 1); e += 2) asm volatile("" : "+v"(pkw[e >> 4][(e & 15) >> 1]));
     }
   };
   // After the last pack: the slow path if some row's terms grew too large.
@@ -509,20 +529,17 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       const bool big = (sum[0][0] + sum[0][1] > kSumLimit) || (sum[1][0] + sum[1][1] > kSumLimit);
       if (__builtin_amdgcn_ballot_w64(big) != 0) {
         float alpha[2];
-        move_reference<kMasked>(scur, w.m, w.l, w.lb, alpha, c, nv8);
+        move_reference<kMasked>(scur, w.m, w.l, alpha, c, nv8);
         w.alpha[0] = alpha[0];
         w.alpha[1] = alpha[1];
         w.rescale = kPV;  // before the first PV product acc is zero: nothing to rescale
         sum[0][0] = sum[0][1] = sum[1][0] = sum[1][1] = 0.0f;
-        sumb[0] = sumb[1] = 0.0f;
         static_for<0, NE>(stage_a);
         static_for<0, NE>(stage_b);
         static_for<0, NE>(stage_c);
       }
       w.l[0] += sum[0][0] + sum[0][1];
       w.l[1] += sum[1][0] + sum[1][1];
-      w.lb[0] += sumb[0];
-      w.lb[1] += sumb[1];
     }
   };
 
@@ -545,6 +562,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       constexpr int pr = s / 2, qb = s % 2;
       constexpr int h = pr / DB, db = pr % DB;
       mfma_o(w.acc[db][qb], vf[pr], pprev[qb][h]);
+      if constexpr (db == 1) mfma_rowsum(w.lbacc[qb], w.sel, pprev[qb][h]);
       // V pairs kVLead pairs ahead of their first slot.
       static_for<0, NPAIR>([&](auto p_tag) {
         constexpr int p = decltype(p_tag)::value;
@@ -658,7 +676,15 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   }
   w.m[0] = w.m[1] = -__builtin_inff();
   w.l[0] = w.l[1] = 0.0f;
-  w.lb[0] = w.lb[1] = 0.0f;
+  w.lbacc[0] = f32x4_t{};
+  w.lbacc[1] = f32x4_t{};
+  {
+    // Selector: lane l holds row l%16 of k-group l/16; 1 where rows 0-7 meet
+    // k-groups 0, 2 and rows 8-15 meet k-groups 1, 3.
+    const bool one = ((lane & 15) < 8) == (((lane >> 4) & 1) == 0);
+    const unsigned word = one ? 0x3F803F80u : 0u;  // two bf16 1.0 or two zeros
+    w.sel = __builtin_bit_cast(bf16x8_t, (u32x4_t){word, word, word, word});
+  }
   w.rescale = false;
   w.alpha[0] = w.alpha[1] = 1.0f;
 #pragma unroll
@@ -747,10 +773,16 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   // it applies to V sum to one exactly; LSE takes the sum of the unrounded terms.
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
+  asm volatile("" : "+v"(w.lbacc[0]), "+v"(w.lbacc[1]));  // read after sync_acc's wait
+  // The rounded-term sum of query q (this lane's q = lane%32) sits in lane q for
+  // q < 16 and lane q + 16 otherwise (see mfma_rowsum).
+  const int q32 = lane & 31;
+  const int lb_src = (q32 < 16 ? q32 : q32 + 16) * 4;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lsum = pair_sum(w.l[qb]);
-    const float inv = 1.0f / pair_sum(w.lb[qb]);
+    const float lbq = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(lb_src, __builtin_bit_cast(int, w.lbacc[qb][0])));
+    const float inv = 1.0f / lbq;
     const int row = q0 + qb * 32 + (lane & 31);
     if (row < N) {
       __bf16* dst = o + head_off + (size_t)row * D;
