@@ -71,6 +71,10 @@ struct Cfg {
   static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
   static constexpr int kKS = D / 16;  // 16-wide k-steps of the QK^T contraction
   static constexpr int kDB = D / 32;  // 32-wide blocks of d in O^T
+  // Offsets from the LDS base of 32-key sub-tile jj's K rows and V rows (jj >= 0;
+  // the stage ring has a period of 2 * kStages sub-tiles).
+  static constexpr int k_tile_off(int jj) { return ((jj >> 1) % kStages) * kStageBytes + (jj & 1) * 32 * kRowBytes; }
+  static constexpr int v_tile_off(int jj) { return k_tile_off(jj) + kTileBytes; }
   static_assert(kLoadsPerTile % kWaves == 0, "tile loads must split evenly over waves");
 };
 
@@ -303,6 +307,8 @@ struct Wave {
   bf16x8_t qf[2][C::kKS];     // Q^T operands (AGPRs)
   unsigned koff[C::kKS];      // LDS addresses of this lane's K operand reads (stage 0, sub-tile 0)
   unsigned voff[C::kDB][2];   // ... and of its V transposing reads (tile base excluded)
+  unsigned koff2[C::kKS];     // the same plus 64 KiB: bases for sub-tiles whose offset exceeds
+  unsigned voff2[C::kDB][2];  // the 16-bit immediate of ds_read
   unsigned gofs[C::kLoadsPerWave];  // this lane's tile_load_offset values
   f32x16_t acc[C::kDB][2];    // O^T accumulator (AGPRs)
   float m[2];                 // reference max, log2 units
@@ -359,7 +365,7 @@ __device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], 
 // issued in the same slot. The softmax runs through the score slots too, so scur
 // and snxt are different registers. kMasked: sub-tile j is the ragged last one (keys >=
 // nvalid, passed as nvalid - 8g, are masked).
-template <int D, bool kPV, bool kExp, bool kQK, bool kMasked>
+template <int D, bool kPV, bool kExp, bool kQK, bool kMasked, int kJ8>
 __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, const char* gk, const char* gv,
                                               LDS_AS char* lds, int wave, int lane, f32x16_t (&scur)[2],
                                               f32x16_t (&snxt)[2], const bf16x8_t (&pprev)[2][2],
@@ -405,8 +411,10 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       w.rescale = false;
     }
   }
+  // kJ8 >= 0: j % 8 is known at compile time, and with it every LDS offset below.
+  const bool odd = kJ8 >= 0 ? (kJ8 & 1) != 0 : (j & 1) != 0;
   if constexpr (kQK) {
-    if (j & 1) {  // sub-tile j+1 opens K/V tile t: wait for it
+    if (odd) {  // sub-tile j+1 opens K/V tile t: wait for it
       static_assert(C::kAhead >= 1 && C::kAhead <= 3, "wait counts below cover up to two later tiles");
       constexpr int kPerTile = 2 * C::kLoadsPerWave;  // this wave's loads per K/V tile
       const int t = (j + 1) >> 1;
@@ -427,29 +435,47 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   // completed in step 2t - 2, before the barrier above.
   // Past the last tile the resource is empty and the loads only zero a free stage.
   const int u_dma = ((j + 1) >> 1) + C::kAhead;
-  const bool dma_v = ((j + 1) & 1) != 0;
+  const bool dma_v = !odd;
   const u32x4_t dma_rsrc = tile_rsrc<D>(dma_v ? gv : gk, u_dma, N);
+  const int dma_stage = kJ8 >= 0 ? (((kJ8 + 1) >> 1) + C::kAhead) % C::kStages : u_dma % C::kStages;
   const unsigned dma_dst = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)lds + (unsigned)((u_dma % C::kStages) * C::kStageBytes + (dma_v ? C::kTileBytes : 0) +
+      (unsigned)(uintptr_t)lds + (unsigned)(dma_stage * C::kStageBytes + (dma_v ? C::kTileBytes : 0) +
                                            wave * C::kLoadsPerWave * 1024));
   __builtin_amdgcn_sched_barrier(0);
 
   // Byte offsets (uniform, SGPR) of this step's sub-tiles from the LDS base: K of
   // j+1, V of j-1, and V of j (read ahead for the next step). readfirstlane: one
   // scalar value each, so every operand address is one v_add.
-  const unsigned kst = __builtin_amdgcn_readfirstlane(
-      kQK ? (unsigned)((((j + 1) >> 1) % C::kStages) * C::kStageBytes + ((j + 1) & 1) * 32 * C::kRowBytes) : 0u);
-  const unsigned vst = __builtin_amdgcn_readfirstlane(
-      kPV ? (unsigned)((((j - 1) >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + ((j - 1) & 1) * 32 * C::kRowBytes)
-          : 0u);
-  const unsigned vnx = __builtin_amdgcn_readfirstlane(
-      kExp ? (unsigned)(((j >> 1) % C::kStages) * C::kStageBytes + C::kTileBytes + (j & 1) * 32 * C::kRowBytes) : 0u);
+  // This step's sub-tiles: K of j+1, V of j-1, V of j (read ahead for the next
+  // step). Scalars when j % 8 is not known at compile time: one v_add per read.
+  const unsigned kst = __builtin_amdgcn_readfirstlane(kQK ? (unsigned)C::k_tile_off(j + 1) : 0u);
+  const unsigned vst = __builtin_amdgcn_readfirstlane(kPV ? (unsigned)C::v_tile_off(j - 1) : 0u);
+  const unsigned vnx = __builtin_amdgcn_readfirstlane(kExp ? (unsigned)C::v_tile_off(j) : 0u);
+  constexpr int kKOff = kJ8 >= 0 ? C::k_tile_off(kJ8 + 1) : 0;
+  constexpr int kVOff = kJ8 >= 0 ? C::v_tile_off(kJ8 + 7) : 0;  // j - 1 (mod 8)
+  constexpr int kVNxOff = kJ8 >= 0 ? C::v_tile_off(kJ8) : 0;
 
-  auto read_v = [&](unsigned base, int pr) -> bf16x8_t {
+  // V^T operand pair pr of the sub-tile at offset `off` (constant) or `base` (scalar).
+  auto read_v = [&](auto off_tag, unsigned base, int pr) -> bf16x8_t {
+    constexpr int off = decltype(off_tag)::value;
     const int h = pr / DB, db = pr % DB;
-    const unsigned b = base + h * 16 * C::kRowBytes;
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(w.voff[db][0] + b));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(w.voff[db][1] + b));
+    unsigned a0, a1;
+    if constexpr (kJ8 >= 0) {
+      // Folded into the 16-bit immediate; the second base set covers offsets past 64 KiB.
+      if (off + h * 16 * C::kRowBytes >= 65536) {
+        a0 = w.voff2[db][0] + (off + h * 16 * C::kRowBytes - 65536);
+        a1 = w.voff2[db][1] + (off + h * 16 * C::kRowBytes - 65536);
+      } else {
+        a0 = w.voff[db][0] + (off + h * 16 * C::kRowBytes);
+        a1 = w.voff[db][1] + (off + h * 16 * C::kRowBytes);
+      }
+    } else {
+      const unsigned b = base + h * 16 * C::kRowBytes;
+      a0 = w.voff[db][0] + b;
+      a1 = w.voff[db][1] + b;
+    }
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)a0);
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)a1);
     return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4,
                                    5, 6, 7);
   };
@@ -457,15 +483,25 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   bf16x8_t vf[NPAIR];
   auto load_k = [&](auto ks_tag) {
     constexpr int ks = decltype(ks_tag)::value;
-    if constexpr (kQK && ks < KS) kf[ks] = *(const LDS_AS bf16x8_t*)(uintptr_t)(w.koff[ks] + kst);
+    if constexpr (kQK && ks < KS) {
+      unsigned a;
+      if constexpr (kJ8 < 0) {
+        a = w.koff[ks] + kst;
+      } else if constexpr (kKOff >= 65536) {
+        a = w.koff2[ks] + (kKOff - 65536);
+      } else {
+        a = w.koff[ks] + kKOff;
+      }
+      kf[ks] = *(const LDS_AS bf16x8_t*)(uintptr_t)a;
+    }
   };
   auto load_v = [&](auto p_tag) {
     constexpr int p = decltype(p_tag)::value;
-    if constexpr (kPV && p >= kVPre && p < NPAIR) vf[p] = read_v(vst, p);
+    if constexpr (kPV && p >= kVPre && p < NPAIR) vf[p] = read_v(std::integral_constant<int, kVOff>{}, vst, p);
   };
   auto prefetch_next = [&](auto p_tag) {
     constexpr int p = decltype(p_tag)::value;
-    if constexpr (kExp && p < kVPre) w.vpre[p] = read_v(vnx, p);
+    if constexpr (kExp && p < kVPre) w.vpre[p] = read_v(std::integral_constant<int, kVNxOff>{}, vnx, p);
   };
   if constexpr (kPV) {
 #pragma unroll
@@ -663,7 +699,12 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   {
     const int r0 = pi_row(lane & 31);
 #pragma unroll
-    for (int ks = 0; ks < C::kKS; ++ks) w.koff[ks] = lds_base + chunk_offset<D>(r0, ks * 2 + g);
+    for (int ks = 0; ks < C::kKS; ++ks) {
+      w.koff[ks] = lds_base + chunk_offset<D>(r0, ks * 2 + g);
+      w.koff2[ks] = w.koff[ks] + 65536u;
+      // Opaque to the compiler, which would otherwise recompute it per read.
+      asm volatile("" : "+v"(w.koff2[ks]));
+    }
   }
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) {
@@ -672,6 +713,8 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
       const int row = 8 * g + 4 * r + ((lane & 15) >> 2);
       const int dcol = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
       w.voff[db][r] = lds_base + chunk_offset<D>(row, dcol >> 3) + 2 * (dcol & 7);
+      w.voff2[db][r] = w.voff[db][r] + 65536u;
+      asm volatile("" : "+v"(w.voff2[db][r]));
     }
   }
   w.m[0] = w.m[1] = -__builtin_inff();
@@ -729,16 +772,28 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
 
   // Step j: PV of j-1, softmax of j, scores of j+1. Two score buffers alternate,
   // so the softmax of j can spread over every MFMA slot of the step.
-#define FA_STEP(PV, EXP, QK, MASK, J, SC, SN, PP, PC) \
-  pipeline_step<D, PV, EXP, QK, MASK>(w, J, T, N, gk, gv, lds, wave, lane, SC, SN, PP, PC, c, nv8)
+#define FA_STEP8(J8, PV, EXP, QK, MASK, J, SC, SN, PP, PC) \
+  pipeline_step<D, PV, EXP, QK, MASK, J8>(w, J, T, N, gk, gv, lds, wave, lane, SC, SN, PP, PC, c, nv8)
+#define FA_STEP(PV, EXP, QK, MASK, J, SC, SN, PP, PC) FA_STEP8(-1, PV, EXP, QK, MASK, J, SC, SN, PP, PC)
   if (U == 1) {
     if (ragged) FA_STEP(false, true, false, true, 0, sa, sb, pb, pa);
     else FA_STEP(false, true, false, false, 0, sa, sb, pb, pa);
   } else {
     FA_STEP(false, true, true, false, 0, sa, sb, pb, pa);
   }
-  // Full steps j = 1 .. U-2, two per iteration.
+  // Full steps j = 1 .. U-2: eight per iteration while they last (j = 1 mod 8
+  // there, so every LDS offset is a compile-time constant), then two at a time.
   int j = 1;
+  for (; j + 7 <= U - 2; j += 8) {
+    FA_STEP8(1, true, true, true, false, j, sb, sa, pa, pb);
+    FA_STEP8(2, true, true, true, false, j + 1, sa, sb, pb, pa);
+    FA_STEP8(3, true, true, true, false, j + 2, sb, sa, pa, pb);
+    FA_STEP8(4, true, true, true, false, j + 3, sa, sb, pb, pa);
+    FA_STEP8(5, true, true, true, false, j + 4, sb, sa, pa, pb);
+    FA_STEP8(6, true, true, true, false, j + 5, sa, sb, pb, pa);
+    FA_STEP8(7, true, true, true, false, j + 6, sb, sa, pa, pb);
+    FA_STEP8(0, true, true, true, false, j + 7, sa, sb, pb, pa);
+  }
   for (; j + 1 <= U - 2; j += 2) {
     FA_STEP(true, true, true, false, j, sb, sa, pa, pb);
     FA_STEP(true, true, true, false, j + 1, sa, sb, pb, pa);
@@ -763,6 +818,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
     FA_STEP(true, false, false, false, 1, sb, sa, pa, pb);
   }
 #undef FA_STEP
+#undef FA_STEP8
 
   // Loads issued after the last tile barrier (zero fills past the last tile) must
   // land before the workgroup's LDS can be handed to another workgroup.
