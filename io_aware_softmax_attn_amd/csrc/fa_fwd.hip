@@ -376,7 +376,10 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   constexpr int NS = NPV + (kQK ? 2 * KS : 0);  // all MFMA slots
   constexpr int NE = 32;                       // score registers per lane (2 blocks x 16)
   // Slots that issue fma work; exp2 and packing trail by one and two slots.
-  constexpr int NAS = NS >= 3 ? NS - 2 : 0;
+  // Each PV slot whose d-block is 1 is followed by a slot of its own for the row-sum
+  // MFMA of the same P^T operand; the softmax work is spread over all slots.
+  constexpr int NT = NS + (kPV ? 4 : 0);
+  constexpr int NAS = NT >= 3 ? NT - 2 : 0;
   constexpr int NPAIR = 2 * DB;                // V^T operand pairs (h, db) of a PV product
   constexpr int kVPre = 4;                     // pairs read in the previous step
   constexpr int kVLead = 4;                    // other pairs: read this many pairs ahead
@@ -544,9 +547,25 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     }
   };
   // Elements whose fma is issued in slot s (s < NAS); exp2 in s+1, pack in s+2.
-  auto a_begin = [](int s) constexpr { return NAS > 0 ? (s * NE) / NAS : 0; };
+  auto a_begin = [](int s) constexpr { return (s * NE) / (NAS > 0 ? NAS : 1); };
   auto softmax_slot = [&](auto s_tag) {
     constexpr int s = decltype(s_tag)::value;
+    // Pin the values entering this slot's fma and exp2 work to the slot start:
+    // scores not yet scaled and scaled scores awaiting exp2. Without these the
+    // instruction scheduler may hoist work of later slots into earlier ones,
+    // overloading those slots. Empty asm: no instructions. (exp2 results are not
+    // pinned: the compiler guards an asm that reads a transcendental's result with
+    // an s_nop, and the packing after them is pinned at its end anyway.)
+    {
+      auto& tvw = tv;  // named here: asm operands alone do not capture in a generic lambda
+      auto& sw = scur;
+      if constexpr (s < NAS && a_begin(s) < 16) asm volatile("" : "+v"(sw[0]));
+      if constexpr (s < NAS && a_begin(s + 1) > 16) asm volatile("" : "+v"(sw[1]));
+      if constexpr (s >= 1) {
+#pragma unroll
+        for (int e = a_begin(s - 1); e < a_begin(s); ++e) asm volatile("" : "+v"(tvw[e >> 4][e & 15]));
+      }
+    }
     if constexpr (s < NAS) static_for<a_begin(s), a_begin(s + 1)>(stage_a);
     if constexpr (s >= 1 && s - 1 < NAS) static_for<a_begin(s - 1), a_begin(s)>(stage_b);
     if constexpr (s >= 2 && s - 2 < NAS) {
@@ -592,13 +611,20 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     finish_softmax();
   }
 
+  // MFMA slot s -> its slot in the timeline that includes the row-sum slots.
+  auto rowsum_after = [](int s) constexpr { return s < NPV && (s / 2) % DB == 1; };
+  auto timeline = [rowsum_after](int s) constexpr {
+    int t = s;
+    for (int x = 0; x < s; ++x) t += rowsum_after(x) ? 1 : 0;
+    return t;
+  };
   static_for<0, NS>([&](auto s_tag) {
     constexpr int s = decltype(s_tag)::value;
+    constexpr int t = timeline(s);
     if constexpr (s < NPV) {
       constexpr int pr = s / 2, qb = s % 2;
       constexpr int h = pr / DB, db = pr % DB;
       mfma_o(w.acc[db][qb], vf[pr], pprev[qb][h]);
-      if constexpr (db == 1) mfma_rowsum(w.lbacc[qb], w.sel, pprev[qb][h]);
       // V pairs kVLead pairs ahead of their first slot.
       static_for<0, NPAIR>([&](auto p_tag) {
         constexpr int p = decltype(p_tag)::value;
@@ -631,10 +657,19 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       }
     }
     if constexpr (kExp && NAS > 0) {
-      softmax_slot(s_tag);
-      if constexpr (s == NAS + 1) finish_softmax();
+      softmax_slot(std::integral_constant<int, t>{});
+      if constexpr (t == NAS + 1) finish_softmax();
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (rowsum_after(s)) {
+      constexpr int qb = s % 2, h = (s / 2) / DB;
+      mfma_rowsum(w.lbacc[qb], w.sel, pprev[qb][h]);
+      if constexpr (kExp && NAS > 0) {
+        softmax_slot(std::integral_constant<int, t + 1>{});
+        if constexpr (t + 1 == NAS + 1) finish_softmax();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   });
   if constexpr (kExp && !kQK) {  // no score slots: read the next step's V operands now
     static_for<0, kVPre>(prefetch_next);
