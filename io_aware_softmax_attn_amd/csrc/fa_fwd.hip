@@ -379,7 +379,11 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   // Each PV slot whose d-block is 1 is followed by a slot of its own for the row-sum
   // MFMA of the same P^T operand; the softmax work is spread over all slots.
   constexpr int NT = NS + (kPV ? 4 : 0);
-  constexpr int NAS = NT >= 3 ? NT - 2 : 0;
+  // The softmax ends kCheckLead slots before the step does: the reference-move
+  // test is taken there and branched on only after the last MFMA, so its
+  // dependence chain (last exp2, sums, compare, ballot) resolves under MFMAs.
+  constexpr int kCheckLead = NT >= 12 ? 2 : 0;
+  constexpr int NAS = NT >= 3 + kCheckLead ? NT - 2 - kCheckLead : 0;
   constexpr int NPAIR = 2 * DB;                // V^T operand pairs (h, db) of a PV product
   constexpr int kVPre = 4;                     // pairs read in the previous step
   constexpr int kVLead = 4;                    // other pairs: read this many pairs ahead
@@ -578,11 +582,18 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       for (int e = a_begin(s - 2) | 1; e < a_begin(s - 1); e += 2) asm volatile("" : "+v"(pkw[e >> 4][(e & 15) >> 1]));
     }
   };
-  // After the last pack: the slow path if some row's terms grew too large.
-  auto finish_softmax = [&]() {
+  // Taken after the step's last MFMA (see check_softmax): the slow path if some
+  // row's terms grew too large.
+  uint64_t big_rows = 0;  // ballot of rows whose terms grew too large
+  auto check_softmax = [&]() {
     if constexpr (kExp) {
       const bool big = (sum[0][0] + sum[0][1] > kSumLimit) || (sum[1][0] + sum[1][1] > kSumLimit);
-      if (__builtin_amdgcn_ballot_w64(big) != 0) {
+      big_rows = __builtin_amdgcn_ballot_w64(big);
+    }
+  };
+  auto finish_softmax = [&]() {
+    if constexpr (kExp) {
+      if (big_rows != 0) {
         float alpha[2];
         move_reference<kMasked>(scur, w.m, w.l, alpha, c, nv8);
         w.alpha[0] = alpha[0];
@@ -608,7 +619,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     static_for<0, NE>(stage_a);
     static_for<0, NE>(stage_b);
     static_for<0, NE>(stage_c);
-    finish_softmax();
+    check_softmax();
   }
 
   // MFMA slot s -> its slot in the timeline that includes the row-sum slots.
@@ -658,7 +669,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     }
     if constexpr (kExp && NAS > 0) {
       softmax_slot(std::integral_constant<int, t>{});
-      if constexpr (t == NAS + 1) finish_softmax();
+      if constexpr (t == NAS + 1) check_softmax();
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (rowsum_after(s)) {
@@ -666,7 +677,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       mfma_rowsum(w.lbacc[qb], w.sel, pprev[qb][h]);
       if constexpr (kExp && NAS > 0) {
         softmax_slot(std::integral_constant<int, t + 1>{});
-        if constexpr (t + 1 == NAS + 1) finish_softmax();
+        if constexpr (t + 1 == NAS + 1) check_softmax();
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -675,6 +686,8 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     static_for<0, kVPre>(prefetch_next);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // After the last MFMA: the slow path if some row's terms grew too large.
+  finish_softmax();
 }
 
 template <int D>
