@@ -523,7 +523,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   float tv[2][16];
-  float sum[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+  float sum[2][2];  // per-lane partial sums of the terms, even and odd registers
   unsigned pk[2][8];  // packed bf16 pairs, assembled into pcur per 8-key operand
   auto stage_a = [&](auto e_tag) {
     constexpr int e = decltype(e_tag)::value, qb = e / 16, i = e % 16;
@@ -539,7 +539,13 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   };
   auto stage_c = [&](auto e_tag) {
     constexpr int e = decltype(e_tag)::value, qb = e / 16, i = e % 16;
-    sum[qb][i & 1] += tv[qb][i];
+    // The first term of each partial sum is assigned, not added to 0: the compiler
+    // may not fold 0 + x (x = -0 would differ), and the terms are never -0.
+    if constexpr (i < 2) {
+      sum[qb][i] = tv[qb][i];
+    } else {
+      sum[qb][i & 1] += tv[qb][i];
+    }
     if constexpr (i & 1) {  // registers i-1, i -> one packed bf16 pair (v_cvt_pk_bf16_f32, nearest-even)
       const bf16x2_t pr = __builtin_convertvector((f32x2_t){tv[qb][i - 1], tv[qb][i]}, bf16x2_t);
       pk[qb][i >> 1] = __builtin_bit_cast(unsigned, pr);
@@ -599,7 +605,6 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
         w.alpha[0] = alpha[0];
         w.alpha[1] = alpha[1];
         w.rescale = kPV;  // before the first PV product acc is zero: nothing to rescale
-        sum[0][0] = sum[0][1] = sum[1][0] = sum[1][1] = 0.0f;
         static_for<0, NE>(stage_a);
         static_for<0, NE>(stage_b);
         static_for<0, NE>(stage_c);
