@@ -515,9 +515,6 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     for (int p = 0; p < kVPre; ++p) vf[p] = w.vpre[p];
   }
 
-  // Wait states between the MFMAs that wrote scur (end of the previous step) and
-  // the VALU reads of it below.
-  if constexpr (kExp) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(scur[0]), "+v"(scur[1]));
 
   // ---- softmax of sub-tile j, staged: fma (A), exp2 (B), sum + pack (C) ----
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -569,7 +566,15 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     {
       auto& tvw = tv;  // named here: asm operands alone do not capture in a generic lambda
       auto& sw = scur;
-      if constexpr (s < NAS && a_begin(s) < 16) asm volatile("" : "+v"(sw[0]));
+      if constexpr (s == 0) {
+        // First VALU read of the scores: after slot 0's MFMA, which cannot issue
+        // before the previous step's last MFMA has run its 32 cycles, so the MFMAs
+        // that wrote scur (issued before that one) have finished. The s_nop adds the
+        // two wait states of a VALU read after an MFMA issue.
+        asm volatile("s_nop 1" : "+v"(sw[0]), "+v"(sw[1]));
+      } else if constexpr (s < NAS && a_begin(s) < 16) {
+        asm volatile("" : "+v"(sw[0]));
+      }
       if constexpr (s < NAS && a_begin(s + 1) > 16) asm volatile("" : "+v"(sw[1]));
       if constexpr (s >= 1) {
 #pragma unroll
