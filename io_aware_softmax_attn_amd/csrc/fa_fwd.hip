@@ -20,16 +20,20 @@
 //    matches the operand layout that ds_read_b64_tr_b16 produces for V^T. The
 //    contraction over keys does not depend on key order.
 //  * 4 waves x 64 query rows per workgroup (BR = 256), 64-key K/V tiles, four
-//    LDS stages filled by direct global->LDS 16-byte loads (global_load_lds_dwordx4)
+//    LDS stages filled by direct global->LDS 16-byte loads (buffer_load_dwordx4
+//    ... lds, through per-tile buffer resources that read rows past N as zero)
 //    with a XOR swizzle of 16-byte chunks against LDS bank conflicts.
 //  * Software pipeline over 32-key sub-tiles: while the matrix cores run the PV
-//    product of sub-tile j-1 and the scores of j+1, the VALU runs the softmax of j.
+//    product of sub-tile j-1 and the scores of j+1, the VALU runs the softmax of j,
+//    one score register per MFMA slot. The main loop is unrolled over the 8-step
+//    period of the LDS ring, so every LDS offset is an instruction immediate.
 //  * exp2 with log2(e) folded into the score scale. The exp2 terms are formed
 //    against the current reference max without a per-tile max; the reference
 //    moves (and the accumulator is rescaled) only when a row's terms over a
 //    sub-tile sum past 2^16. Any reference gives the same O and LSE in exact
 //    arithmetic; O is divided by the sum of the bf16-rounded terms that built the
-//    accumulator, so the weights applied to V sum to one whatever the reference.
+//    accumulator (computed on the matrix cores), so the weights applied to V sum
+//    to one whatever the reference.
 //  * Workgroup ids are remapped so that each XCD (8 per chip, dispatched
 //    round-robin) runs consecutive query tiles of the same head, keeping that
 //    head's K/V hot in the XCD's L2.
@@ -48,7 +52,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -199,17 +202,16 @@ __device__ __forceinline__ void dma16(u32x4_t rsrc, unsigned voff, unsigned lds_
 }
 
 // Issue this wave's loads of K tile u (kV = false) or V tile u (kV = true) of one
-// head into `stage`, loads i0 .. i1-1. gofs holds this lane's tile_load_offset values.
+// head into `stage`. gofs holds this lane's tile_load_offset values.
 template <int D, bool kV>
 __device__ __forceinline__ void issue_half(const char* __restrict__ head, int u, int N, unsigned stage, int wave,
-                                           const unsigned* gofs, int i0, int i1) {
+                                           const unsigned* gofs) {
   using C = Cfg<D>;
   const u32x4_t r = tile_rsrc<D>(head, u, N);
   const unsigned dst = __builtin_amdgcn_readfirstlane(stage + (kV ? C::kTileBytes : 0) +
                                                       (unsigned)(wave * C::kLoadsPerWave * 1024));
 #pragma unroll
-  for (int i = 0; i < C::kLoadsPerWave; ++i)
-    if (i >= i0 && i < i1) dma16(r, gofs[i], dst + i * 1024);
+  for (int i = 0; i < C::kLoadsPerWave; ++i) dma16(r, gofs[i], dst + i * 1024);
 }
 
 // ---------------------------------------------------------------------------
@@ -217,9 +219,10 @@ __device__ __forceinline__ void issue_half(const char* __restrict__ head, int u,
 // softmax reads them with VALU instructions); the output accumulator O^T lives
 // in AGPRs for the whole kernel (only MFMAs and the rare rescale touch it). The
 // compiler does not see these as MFMAs, so the code below keeps the required
-// wait states itself: S is read by VALU code at least 16 MFMAs after it was
-// written, P is written at least one step before the MFMA that reads it, and
-// every VALU access to O^T goes through sync_acc() first.
+// wait states itself: S is first read by VALU code after the next step's first
+// MFMA (see the slot-0 s_nop in pipeline_step), P is written at least one step
+// before the MFMA that reads it, and every VALU access to O^T goes through
+// sync_acc() first.
 // Scores: the Q^T operand (b) stays in AGPRs too, as the MFMA B source.
 __device__ __forceinline__ void mfma_s(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
@@ -250,42 +253,6 @@ __device__ __forceinline__ void mfma_rowsum(f32x4_t& d, bf16x8_t& sel, const bf1
 // Wait states between the last MFMA that wrote an accumulator and VALU reads of it.
 __device__ __forceinline__ void sync_acc(f32x16_t& a, f32x16_t& b) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(a), "+a"(b));
-}
-
-// acc *= alpha, in place in AGPRs, when flag != 0 (VALU cannot read AGPRs, so
-// each element goes through a VGPR). The branch lives inside the asm so that the
-// compiler sees one unconditional definition of acc and keeps it in the same
-// AGPRs. The s_nops cover the wait states after the MFMA that last wrote acc and
-// before the next MFMA reads it.
-__device__ __forceinline__ void scale_agpr_if(f32x16_t& a, float alpha, unsigned flag) {
-  float t;
-  asm volatile(
-      "s_cmp_eq_u32 %18, 0\n\t"
-      "s_cbranch_scc1 .Lskip_scale%=\n\t"
-      "s_nop 15\n\ts_nop 15\n\ts_nop 15\n\t"
-      "v_accvgpr_read_b32 %16, %0\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %0, %16\n\t"
-      "v_accvgpr_read_b32 %16, %1\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %1, %16\n\t"
-      "v_accvgpr_read_b32 %16, %2\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %2, %16\n\t"
-      "v_accvgpr_read_b32 %16, %3\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %3, %16\n\t"
-      "v_accvgpr_read_b32 %16, %4\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %4, %16\n\t"
-      "v_accvgpr_read_b32 %16, %5\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %5, %16\n\t"
-      "v_accvgpr_read_b32 %16, %6\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %6, %16\n\t"
-      "v_accvgpr_read_b32 %16, %7\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %7, %16\n\t"
-      "v_accvgpr_read_b32 %16, %8\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %8, %16\n\t"
-      "v_accvgpr_read_b32 %16, %9\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %9, %16\n\t"
-      "v_accvgpr_read_b32 %16, %10\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %10, %16\n\t"
-      "v_accvgpr_read_b32 %16, %11\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %11, %16\n\t"
-      "v_accvgpr_read_b32 %16, %12\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %12, %16\n\t"
-      "v_accvgpr_read_b32 %16, %13\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %13, %16\n\t"
-      "v_accvgpr_read_b32 %16, %14\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %14, %16\n\t"
-      "v_accvgpr_read_b32 %16, %15\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %15, %16\n\t"
-      "s_nop 7\n"
-      ".Lskip_scale%=:"
-      : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]), "+a"(a[6]), "+a"(a[7]),
-        "+a"(a[8]), "+a"(a[9]), "+a"(a[10]), "+a"(a[11]), "+a"(a[12]), "+a"(a[13]), "+a"(a[14]), "+a"(a[15]),
-        "=&v"(t)
-      : "v"(alpha), "s"(flag)
-      : "scc");
 }
 
 // Key index, within a 32-key sub-tile, of S^T accumulator register i, minus 8g:
@@ -359,12 +326,13 @@ __device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], 
 // exact arithmetic the result does not depend on the reference. In rounded
 // arithmetic the terms' bf16 rounding does; dividing O by the sum of the rounded
 // terms (lb) rather than of the exact ones cancels it for the terms that dominate
-// a row, whatever the reference. The work is staged over the PV slots:
-// slot s issues the fma of some registers, the exp2 of those of slot s-1 and the
-// sum and bf16 packing of those of slot s-2, so no instruction waits for one
-// issued in the same slot. The softmax runs through the score slots too, so scur
-// and snxt are different registers. kMasked: sub-tile j is the ragged last one (keys >=
-// nvalid, passed as nvalid - 8g, are masked).
+// a row, whatever the reference. The work is staged over all MFMA slots of the
+// step (PV, row-sum and score slots): slot s issues the fma of one score
+// register, the exp2 of the register of slot s-1 and the sum and bf16 packing of
+// the register of slot s-2, so no instruction waits for one issued in the same
+// slot. scur and snxt are different registers (the scores of j+1 are written while
+// those of j are read). kMasked: sub-tile j is the ragged last one (keys >= nvalid,
+// passed as nvalid - 8g, are masked). kJ8 >= 0: j % 8 is known at compile time.
 template <int D, bool kPV, bool kExp, bool kQK, bool kMasked, int kJ8>
 __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, const char* gk, const char* gv,
                                               LDS_AS char* lds, int wave, int lane, f32x16_t (&scur)[2],
@@ -732,8 +700,8 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   }
   // Start streaming K/V tile 0 while Q is loaded.
   const unsigned lds_u = (unsigned)(uintptr_t)lds;
-  issue_half<D, false>(gk, 0, N, lds_u, wave, w.gofs, 0, C::kLoadsPerWave);
-  issue_half<D, true>(gv, 0, N, lds_u, wave, w.gofs, 0, C::kLoadsPerWave);
+  issue_half<D, false>(gk, 0, N, lds_u, wave, w.gofs);
+  issue_half<D, true>(gv, 0, N, lds_u, wave, w.gofs);
 
   // Q^T operand fragments: lane holds query q0 + qb*32 + lane%32, d = ks*16 + g*8 .. +8.
 #pragma unroll
@@ -801,8 +769,8 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
 #pragma unroll
   for (int t = 1; t <= C::kAhead; ++t) {
     if (t < T) {
-      issue_half<D, false>(gk, t, N, lds_u + t * C::kStageBytes, wave, w.gofs, 0, C::kLoadsPerWave);
-      if (t < C::kAhead) issue_half<D, true>(gv, t, N, lds_u + t * C::kStageBytes, wave, w.gofs, 0, C::kLoadsPerWave);
+      issue_half<D, false>(gk, t, N, lds_u + t * C::kStageBytes, wave, w.gofs);
+      if (t < C::kAhead) issue_half<D, true>(gv, t, N, lds_u + t * C::kStageBytes, wave, w.gofs);
     }
   }
 
@@ -839,6 +807,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   } else {
     FA_STEP(false, true, true, false, 0, sa, sb, pb, pa);
   }
+  static_assert(2 * C::kStages == 8, "the eight-step loop below covers one period of the LDS stage ring");
   // Full steps j = 1 .. U-2: eight per iteration while they last (j = 1 mod 8
   // there, so every LDS offset is a compile-time constant), then two at a time.
   int j = 1;
