@@ -326,11 +326,10 @@ __device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], 
 // exact arithmetic the result does not depend on the reference. In rounded
 // arithmetic the terms' bf16 rounding does; dividing O by the sum of the rounded
 // terms (lb) rather than of the exact ones cancels it for the terms that dominate
-// a row, whatever the reference. The work is staged over all MFMA slots of the
-// step (PV, row-sum and score slots): slot s issues the fma of one score
-// register, the exp2 of the register of slot s-1 and the sum and bf16 packing of
-// the register of slot s-2, so no instruction waits for one issued in the same
-// slot. scur and snxt are different registers (the scores of j+1 are written while
+// a row, whatever the reference. The work is staged over the step's PV and score
+// MFMA slots: slot s issues the fma of about one score register, the exp2 of those
+// of slot s-1 and the sum and bf16 packing of those of slot s-2, so no instruction
+// waits for one issued in the same slot. scur and snxt are different registers (the scores of j+1 are written while
 // those of j are read). kMasked: sub-tile j is the ragged last one (keys >= nvalid,
 // passed as nvalid - 8g, are masked). kJ8 >= 0: j % 8 is known at compile time.
 template <int D, bool kPV, bool kExp, bool kQK, bool kMasked, int kJ8>
@@ -343,15 +342,15 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   constexpr int NPV = kPV ? 4 * DB : 0;        // MFMA slots of the PV product (first)
   constexpr int NS = NPV + (kQK ? 2 * KS : 0);  // all MFMA slots
   constexpr int NE = 32;                       // score registers per lane (2 blocks x 16)
-  // Slots that issue fma work; exp2 and packing trail by one and two slots.
-  // Each PV slot whose d-block is 1 is followed by a slot of its own for the row-sum
-  // MFMA of the same P^T operand; the softmax work is spread over all slots.
-  constexpr int NT = NS + (kPV ? 4 : 0);
-  // The softmax ends kCheckLead slots before the step does: the reference-move
-  // test is taken there and branched on only after the last MFMA, so its
-  // dependence chain (last exp2, sums, compare, ballot) resolves under MFMAs.
-  constexpr int kCheckLead = NT >= 12 ? 2 : 0;
-  constexpr int NAS = NT >= 3 + kCheckLead ? NT - 2 - kCheckLead : 0;
+  // The softmax is staged over the NS MFMA slots: NAS slots issue fma work, exp2
+  // and packing trail by one and two slots. Each PV slot whose d-block is 1 is
+  // followed by a row-sum MFMA of the same P^T operand (16x16x32, half as long),
+  // which carries no softmax work of its own. The softmax ends kCheckLead slots
+  // before the step does: the reference-move test is taken there and branched on
+  // only after the last MFMA, so its dependence chain (last exp2, sums, compare,
+  // ballot) resolves under MFMAs.
+  constexpr int kCheckLead = NS >= 12 ? 2 : 0;
+  constexpr int NAS = NS >= 3 + kCheckLead ? NS - 2 - kCheckLead : 0;
   constexpr int NPAIR = 2 * DB;                // V^T operand pairs (h, db) of a PV product
   constexpr int kVPre = 4;                     // pairs read in the previous step
   constexpr int kVLead = 4;                    // other pairs: read this many pairs ahead
@@ -600,16 +599,10 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     check_softmax();
   }
 
-  // MFMA slot s -> its slot in the timeline that includes the row-sum slots.
+  // PV slots whose d-block is 1 are followed by the row-sum MFMA of their P^T operand.
   auto rowsum_after = [](int s) constexpr { return s < NPV && (s / 2) % DB == 1; };
-  auto timeline = [rowsum_after](int s) constexpr {
-    int t = s;
-    for (int x = 0; x < s; ++x) t += rowsum_after(x) ? 1 : 0;
-    return t;
-  };
   static_for<0, NS>([&](auto s_tag) {
     constexpr int s = decltype(s_tag)::value;
-    constexpr int t = timeline(s);
     if constexpr (s < NPV) {
       constexpr int pr = s / 2, qb = s % 2;
       constexpr int h = pr / DB, db = pr % DB;
@@ -646,17 +639,13 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       }
     }
     if constexpr (kExp && NAS > 0) {
-      softmax_slot(std::integral_constant<int, t>{});
-      if constexpr (t == NAS + 1) check_softmax();
+      softmax_slot(std::integral_constant<int, s>{});
+      if constexpr (s == NAS + 1) check_softmax();
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (rowsum_after(s)) {
       constexpr int qb = s % 2, h = (s / 2) / DB;
       mfma_rowsum(w.lbacc[qb], w.sel, pprev[qb][h]);
-      if constexpr (kExp && NAS > 0) {
-        softmax_slot(std::integral_constant<int, t + 1>{});
-        if constexpr (t + 1 == NAS + 1) check_softmax();
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
   });
