@@ -24,6 +24,8 @@
  *     the uniform average).
  *   - Q, K, V, O must be 16-byte aligned; LSE 4-byte aligned. Q, K and V may
  *     share memory; O and LSE must not overlap any input or each other.
+ *   - Work is launched on the calling thread's current HIP device; the tensors
+ *     and the stream must belong to it.
  *   - stream is a hipStream_t passed as void* (NULL = the null stream). Calls
  *     are asynchronous: they return after enqueueing the work; faults during
  *     execution surface at the caller's next synchronisation on that stream.

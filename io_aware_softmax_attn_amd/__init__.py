@@ -105,10 +105,16 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else t.data_ptr()
 
 
-def _stream_handle(stream) -> int | None:
+def _stream_handle(stream, device) -> int | None:
+    """The hipStream_t to enqueue on: ``stream`` (a torch stream or a raw handle), or
+    torch's current stream of ``device``. A torch stream must belong to ``device``."""
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        stream = torch.cuda.current_stream(device)
+    if hasattr(stream, "cuda_stream"):
+        if getattr(stream, "device", device) != device:
+            raise ValueError(f"stream is on {stream.device}, tensors are on {device}")
+        return stream.cuda_stream
+    return int(stream)
 
 
 def _shape_of(q, k, v, o, lse):
@@ -122,6 +128,8 @@ def _shape_of(q, k, v, o, lse):
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    if len({t.device for t in (q, k, v, o, lse)}) != 1:
+        raise ValueError("q, k, v, o and lse must be on the same GPU")
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or o.shape != q.shape:
         raise ValueError("q, k, v, o must all have shape [B, H, N, d]")
     if tuple(lse.shape) != tuple(q.shape[:3]):
@@ -135,8 +143,9 @@ def fa_fwd(q, k, v, o, lse, scale=None, stream=None):
     B, H, N, d = _shape_of(q, k, v, o, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    _raise(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
-                      _stream_handle(stream)), "fa_fwd")
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        _raise(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                          _stream_handle(stream, q.device)), "fa_fwd")
     return o, lse
 
 
@@ -148,9 +157,12 @@ def fa_unfused_fwd(q, k, v, o, lse, workspace, scale=None, stream=None):
         scale = 1.0 / math.sqrt(d)
     if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
+    if workspace.device != q.device:
+        raise ValueError("workspace must be on the same GPU as the tensors")
     nbytes = workspace.numel() * workspace.element_size()
-    _raise(lib.fa_unfused_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
-                              _ptr(workspace), nbytes, _stream_handle(stream)), "fa_unfused_fwd")
+    with torch.cuda.device(q.device):
+        _raise(lib.fa_unfused_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                  _ptr(workspace), nbytes, _stream_handle(stream, q.device)), "fa_unfused_fwd")
     return o, lse
 
 
