@@ -208,3 +208,20 @@ def test_argument_errors_raise(fa):
         fa.fa_fwd(q, k, v, o, lse, scale=float("nan"))
     with pytest.raises(ValueError):
         fa.fa_fwd(q, k, v, o, lse, scale=-1.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_v_power_of_two_scaling_is_exact(fa, d):
+    """O is linear in V and LSE does not depend on it, so scaling V by 2^100 (exact
+    in bf16) must scale O by exactly 2^100 and leave LSE bit-identical. Values near
+    1e30 also exercise the headroom the lazy reference leaves (exp2 terms up to
+    2^16 per sub-tile, so |acc| <= 2^12 * N * max|V|)."""
+    N = 1000
+    announce(f"V scaled by 2^100 N={N} d={d}")
+    q, k, v = attn_inputs.make_qkv(1, 2, N, d, seed=15, sigma_qk=2.0)
+    o1, l1 = run_fused(fa, q, k, v, default_scale(d))
+    vs = (v.float() * 2.0 ** 100).to(torch.bfloat16)
+    assert torch.equal(vs.float() / 2.0 ** 100, v.float())  # the scaling is exact
+    o2, l2 = run_fused(fa, q, k, vs, default_scale(d))
+    assert torch.equal(l1, l2)
+    assert torch.equal(o2.float(), (o1.float() * 2.0 ** 100).to(torch.bfloat16).float())
