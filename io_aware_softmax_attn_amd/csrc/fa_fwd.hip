@@ -850,26 +850,43 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   // q < 16 and lane q + 16 otherwise (see mfma_rowsum).
   const int q32 = lane & 31;
   const int lb_src = (q32 < 16 ? q32 : q32 + 16) * 4;
+  // O goes through LDS: each lane holds 8-byte pieces of 32 different rows, so
+  // storing it directly would take 32 scattered stores per lane. Written into a
+  // row-major tile of this wave's 64 rows (row pitch padded by 16 bytes against
+  // bank conflicts) and read back by rows, it leaves as 16 fully coalesced 16-byte
+  // stores per lane. The K/V stages are idle by then: the barrier waits until every
+  // wave has finished its last step (and, with the vmem wait above, every load).
+  __syncthreads();
+  constexpr int kOPitch = D * 2 + 16;
+  static_assert(C::kWaves * 64 * kOPitch <= C::kLdsBytes, "O staging tiles must fit in the K/V stages");
+  const unsigned otile = (unsigned)(uintptr_t)lds + (unsigned)(wave * 64 * kOPitch);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lsum = pair_sum(w.l[qb]);
     const float lbq = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(lb_src, __builtin_bit_cast(int, w.lbacc[qb][0])));
     const float inv = 1.0f / lbq;
-    const int row = q0 + qb * 32 + (lane & 31);
-    if (row < N) {
-      __bf16* dst = o + head_off + (size_t)row * D;
+    const unsigned rbase = otile + (unsigned)((qb * 32 + (lane & 31)) * kOPitch + 8 * g);
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
+    for (int db = 0; db < C::kDB; ++db) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4_t wv;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4_t wv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) wv[e] = (__bf16)(w.acc[db][qb][i4 * 4 + e] * inv);
-          *(bf16x4_t*)(dst + db * 32 + 8 * i4 + 4 * g) = wv;
-        }
+        for (int e = 0; e < 4; ++e) wv[e] = (__bf16)(w.acc[db][qb][i4 * 4 + e] * inv);
+        *(LDS_AS bf16x4_t*)(uintptr_t)(rbase + (unsigned)((db * 32 + 8 * i4) * 2)) = wv;
       }
-      if (g == 0) lse[(size_t)bh * N + row] = kLn2 * (w.m[qb] + log2f(lsum));
     }
+    const int row = q0 + qb * 32 + (lane & 31);
+    if (g == 0 && row < N) lse[(size_t)bh * N + row] = kLn2 * (w.m[qb] + log2f(lsum));
+  }
+  // Read back by rows: 16-byte chunk c = lane + 64*k is row c / kChunks, chunk c % kChunks.
+  constexpr int kRowsPerPass = 64 / C::kChunks;
+#pragma unroll
+  for (int k = 0; k < C::kChunks; ++k) {
+    const int r = k * kRowsPerPass + lane / C::kChunks, ch = lane % C::kChunks;
+    const bf16x8_t x = *(const LDS_AS bf16x8_t*)(uintptr_t)(otile + (unsigned)(r * kOPitch + ch * 16));
+    const int row = q0 + r;
+    if (row < N) *(bf16x8_t*)(o + head_off + (size_t)row * D + ch * 8) = x;
   }
 }
 
