@@ -331,8 +331,9 @@ __device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], 
 // of slot s-1 and the sum and bf16 packing of those of slot s-2, so no instruction
 // waits for one issued in the same slot. scur and snxt are different registers (the scores of j+1 are written while
 // those of j are read). kMasked: sub-tile j is the ragged last one (keys >= nvalid,
-// passed as nvalid - 8g, are masked). kJ8 >= 0: j % 8 is known at compile time.
-template <int D, bool kPV, bool kExp, bool kQK, bool kMasked, int kJ8>
+// passed as nvalid - 8g, are masked). kJP >= 0: j mod the ring period (2 * kStages)
+// is known at compile time.
+template <int D, bool kPV, bool kExp, bool kQK, bool kMasked, int kJP>
 __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, const char* gk, const char* gv,
                                               LDS_AS char* lds, int wave, int lane, f32x16_t (&scur)[2],
                                               f32x16_t (&snxt)[2], const bf16x8_t (&pprev)[2][2],
@@ -385,8 +386,9 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
       w.rescale = false;
     }
   }
-  // kJ8 >= 0: j % 8 is known at compile time, and with it every LDS offset below.
-  const bool odd = kJ8 >= 0 ? (kJ8 & 1) != 0 : (j & 1) != 0;
+  // kJP >= 0: j mod the ring period is known at compile time, and with it every LDS
+  // offset below.
+  const bool odd = kJP >= 0 ? (kJP & 1) != 0 : (j & 1) != 0;
   if constexpr (kQK) {
     if (odd) {  // sub-tile j+1 opens K/V tile t: wait for it
       static_assert(C::kAhead >= 1 && C::kAhead <= 3, "wait counts below cover up to two later tiles");
@@ -411,7 +413,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   const int u_dma = ((j + 1) >> 1) + C::kAhead;
   const bool dma_v = !odd;
   const u32x4_t dma_rsrc = tile_rsrc<D>(dma_v ? gv : gk, u_dma, N);
-  const int dma_stage = kJ8 >= 0 ? (((kJ8 + 1) >> 1) + C::kAhead) % C::kStages : u_dma % C::kStages;
+  const int dma_stage = kJP >= 0 ? (((kJP + 1) >> 1) + C::kAhead) % C::kStages : u_dma % C::kStages;
   const unsigned dma_dst = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)lds + (unsigned)(dma_stage * C::kStageBytes + (dma_v ? C::kTileBytes : 0) +
                                            wave * C::kLoadsPerWave * 1024));
@@ -425,16 +427,16 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   const unsigned kst = __builtin_amdgcn_readfirstlane(kQK ? (unsigned)C::k_tile_off(j + 1) : 0u);
   const unsigned vst = __builtin_amdgcn_readfirstlane(kPV ? (unsigned)C::v_tile_off(j - 1) : 0u);
   const unsigned vnx = __builtin_amdgcn_readfirstlane(kExp ? (unsigned)C::v_tile_off(j) : 0u);
-  constexpr int kKOff = kJ8 >= 0 ? C::k_tile_off(kJ8 + 1) : 0;
-  constexpr int kVOff = kJ8 >= 0 ? C::v_tile_off(kJ8 + 7) : 0;  // j - 1 (mod 8)
-  constexpr int kVNxOff = kJ8 >= 0 ? C::v_tile_off(kJ8) : 0;
+  constexpr int kKOff = kJP >= 0 ? C::k_tile_off(kJP + 1) : 0;
+  constexpr int kVOff = kJP >= 0 ? C::v_tile_off(kJP + 2 * C::kStages - 1) : 0;  // j - 1 (mod the period)
+  constexpr int kVNxOff = kJP >= 0 ? C::v_tile_off(kJP) : 0;
 
   // V^T operand pair pr of the sub-tile at offset `off` (constant) or `base` (scalar).
   auto read_v = [&](auto off_tag, unsigned base, int pr) -> bf16x8_t {
     constexpr int off = decltype(off_tag)::value;
     const int h = pr / DB, db = pr % DB;
     unsigned a0, a1;
-    if constexpr (kJ8 >= 0) {
+    if constexpr (kJP >= 0) {
       // Folded into the 16-bit immediate; the second base set covers offsets past 64 KiB.
       if (off + h * 16 * C::kRowBytes >= 65536) {
         a0 = w.voff2[db][0] + (off + h * 16 * C::kRowBytes - 65536);
@@ -459,7 +461,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     constexpr int ks = decltype(ks_tag)::value;
     if constexpr (kQK && ks < KS) {
       unsigned a;
-      if constexpr (kJ8 < 0) {
+      if constexpr (kJP < 0) {
         a = w.koff[ks] + kst;
       } else if constexpr (kKOff >= 65536) {
         a = w.koff2[ks] + (kKOff - 65536);
@@ -787,28 +789,29 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
 
   // Step j: PV of j-1, softmax of j, scores of j+1. Two score buffers alternate,
   // so the softmax of j can spread over every MFMA slot of the step.
-#define FA_STEP8(J8, PV, EXP, QK, MASK, J, SC, SN, PP, PC) \
-  pipeline_step<D, PV, EXP, QK, MASK, J8>(w, J, T, N, gk, gv, lds, wave, lane, SC, SN, PP, PC, c, nv8)
-#define FA_STEP(PV, EXP, QK, MASK, J, SC, SN, PP, PC) FA_STEP8(-1, PV, EXP, QK, MASK, J, SC, SN, PP, PC)
+#define FA_STEPP(JP, PV, EXP, QK, MASK, J, SC, SN, PP, PC) \
+  pipeline_step<D, PV, EXP, QK, MASK, JP>(w, J, T, N, gk, gv, lds, wave, lane, SC, SN, PP, PC, c, nv8)
+#define FA_STEP(PV, EXP, QK, MASK, J, SC, SN, PP, PC) FA_STEPP(-1, PV, EXP, QK, MASK, J, SC, SN, PP, PC)
   if (U == 1) {
     if (ragged) FA_STEP(false, true, false, true, 0, sa, sb, pb, pa);
     else FA_STEP(false, true, false, false, 0, sa, sb, pb, pa);
   } else {
     FA_STEP(false, true, true, false, 0, sa, sb, pb, pa);
   }
-  static_assert(2 * C::kStages == 8, "the eight-step loop below covers one period of the LDS stage ring");
-  // Full steps j = 1 .. U-2: eight per iteration while they last (j = 1 mod 8
-  // there, so every LDS offset is a compile-time constant), then two at a time.
+  // Full steps j = 1 .. U-2: one period of the LDS stage ring (2 * kStages steps)
+  // per iteration while they last (j = 1 mod the period there, so every LDS offset
+  // is a compile-time constant), then two at a time.
+  constexpr int kPeriod = 2 * C::kStages;
   int j = 1;
-  for (; j + 7 <= U - 2; j += 8) {
-    FA_STEP8(1, true, true, true, false, j, sb, sa, pa, pb);
-    FA_STEP8(2, true, true, true, false, j + 1, sa, sb, pb, pa);
-    FA_STEP8(3, true, true, true, false, j + 2, sb, sa, pa, pb);
-    FA_STEP8(4, true, true, true, false, j + 3, sa, sb, pb, pa);
-    FA_STEP8(5, true, true, true, false, j + 4, sb, sa, pa, pb);
-    FA_STEP8(6, true, true, true, false, j + 5, sa, sb, pb, pa);
-    FA_STEP8(7, true, true, true, false, j + 6, sb, sa, pa, pb);
-    FA_STEP8(0, true, true, true, false, j + 7, sa, sb, pb, pa);
+  for (; j + kPeriod - 1 <= U - 2; j += kPeriod) {
+    static_for<0, kPeriod>([&](auto i_tag) {
+      constexpr int i = decltype(i_tag)::value;  // step j + i; odd when i is even
+      if constexpr (i % 2 == 0) {
+        FA_STEPP((i + 1) % kPeriod, true, true, true, false, j + i, sb, sa, pa, pb);
+      } else {
+        FA_STEPP((i + 1) % kPeriod, true, true, true, false, j + i, sa, sb, pb, pa);
+      }
+    });
   }
   for (; j + 1 <= U - 2; j += 2) {
     FA_STEP(true, true, true, false, j, sb, sa, pa, pb);
@@ -834,7 +837,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
     FA_STEP(true, false, false, false, 1, sb, sa, pa, pb);
   }
 #undef FA_STEP
-#undef FA_STEP8
+#undef FA_STEPP
 
   // Loads issued after the last tile barrier (zero fills past the last tile) must
   // land before the workgroup's LDS can be handed to another workgroup.
