@@ -318,10 +318,10 @@ __device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], 
 // pcur), so no MFMA depends on a VALU result of the same step.
 //
 // Softmax: the exp2 terms are formed against the current reference max m without
-// computing the tile max first. If some row's sum of terms over the sub-tile
-// exceeds 2^16 (or is infinite: the first sub-tile, where m = -inf), the wave
-// takes a slow path that moves the reference to the row max (move_reference),
-// schedules the accumulator rescale for the next step and recomputes the terms.
+// computing the tile max first (the reference starts at sub-tile 0's row max). If
+// some row's sum of terms over the sub-tile exceeds 2^16, the wave takes a slow
+// path that moves the reference to the row max (move_reference), schedules the
+// accumulator rescale for the next step and recomputes the terms.
 // Otherwise every term is at most 2^16, far inside fp32 and bf16 range, and in
 // exact arithmetic the result does not depend on the reference. In rounded
 // arithmetic the terms' bf16 rounding does; dividing O by the sum of the rounded
@@ -785,6 +785,13 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
       }
     }
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(sa[0]), "+v"(sa[1]));
+  }
+  // The reference max starts at sub-tile 0's row max (move_reference from m = -inf:
+  // alpha = 0 and l stays 0), so the first softmax step takes the fast path.
+  {
+    float alpha0[2];
+    if (U == 1 && ragged) move_reference<true>(sa, w.m, w.l, alpha0, c, nv8);
+    else move_reference<false>(sa, w.m, w.l, alpha0, c, nv8);
   }
 
   // Step j: PV of j-1, softmax of j, scores of j+1. Two score buffers alternate,
