@@ -6,6 +6,7 @@ in HBM before the timed region. Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--unfused] [--launches-only]
+  python bench.py --memory OUT_MD      (peak device memory, fused vs unfused)
 
 The roofline entry is measured live: per-launch HIP events recorded on the stream
 the kernel runs on, averaged over the timed region. Its ``traffic`` field comes
@@ -190,6 +191,77 @@ def summarize_trace(stats_csv, command, workload):
     print("\n".join(lines))
 
 
+# Shapes of the device-memory comparison: (B, H, d, sequence lengths).
+MEMORY_SHAPES = ((2, 16, 128, (1024, 2048, 4096, 8192)), (4, 16, 64, (1024, 2048, 4096, 8192)))
+
+
+def footprint_bytes(B: int, H: int, N: int, d: int, fused: bool) -> int:
+    """Device bytes one forward holds at its peak: Q, K, V and O (bf16) and LSE
+    (fp32), plus, on the unfused path, the score matrix S (fp32) and the
+    probabilities P (bf16) of every head. The fused footprint grows with N, the
+    unfused one with N^2 ("01 · 注意力为什么是 IO 瓶颈", section 6: the memory saved
+    at 2K and 4K sequence length, growing linearly with it)."""
+    base = B * H * N * (8 * d + 4)
+    return base if fused else base + 6 * B * H * N * N
+
+
+def memory_comparison(out_md: str, command: str):
+    """Peak device memory of one fused and one unfused forward per shape, measured
+    with torch's allocator statistics (the library itself allocates nothing; O, LSE
+    and the unfused workspace come from torch), next to footprint_bytes."""
+    import torch
+
+    import attn_inputs
+    import io_aware_softmax_attn_amd as fa
+
+    dev = torch.device("cuda:0")
+    recs = []
+    for B, H, d, lengths in MEMORY_SHAPES:
+        for N in lengths:
+            q, k, v = (t.to(dev) for t in attn_inputs.make_qkv(B, H, N, d, seed=N))
+            rec = {"B": B, "H": H, "N": N, "d": d}
+            for path, fn in (("fused", fa.forward), ("unfused", fa.unfused_forward)):
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+                torch.cuda.reset_peak_memory_stats(dev)
+                outs = fn(q, k, v)
+                torch.cuda.synchronize()
+                # Requested bytes: the tensors' own sizes, before the allocator rounds
+                # them to its blocks (the rounded peak is kept for reference).
+                rec[f"{path}_peak_bytes"] = torch.cuda.memory_stats(dev)["requested_bytes.all.peak"]
+                rec[f"{path}_peak_block_bytes"] = torch.cuda.max_memory_allocated(dev)
+                rec[f"{path}_model_bytes"] = footprint_bytes(B, H, N, d, path == "fused")
+                del outs
+            rec["ratio"] = rec["unfused_peak_bytes"] / rec["fused_peak_bytes"]
+            del q, k, v
+            recs.append(rec)
+            print(json.dumps(rec), flush=True)
+    lines = [
+        "# Peak device memory of one forward, fused vs unfused",
+        "",
+        "Command, run from the repository root:",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "Peak requested bytes from torch.cuda.memory_stats around one call, with Q, K and V already resident. "
+        "The model column is B*H*N*(8d+4) for the fused path (Q, K, V, O, LSE) plus 6*B*H*N^2 for the "
+        "unfused path's S (fp32) and P (bf16).",
+        "",
+        "| B | H | N | d | fused MiB | unfused MiB | unfused / fused | both equal the model |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    for r in recs:
+        ok = r["fused_peak_bytes"] == r["fused_model_bytes"] and r["unfused_peak_bytes"] == r["unfused_model_bytes"]
+        lines.append(f"| {r['B']} | {r['H']} | {r['N']} | {r['d']} | {r['fused_peak_bytes'] / 2**20:.1f} | "
+                     f"{r['unfused_peak_bytes'] / 2**20:.1f} | {r['ratio']:.1f}x | {'yes' if ok else 'no'} |")
+    os.makedirs(os.path.dirname(os.path.abspath(out_md)), exist_ok=True)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return recs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +281,9 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="no GPU work: turn a rocprofv3 --kernel-trace --stats kernel_stats.csv into "
                          "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin")
+    ap.add_argument("--memory", metavar="OUT_MD",
+                    help="instead of timing: peak device memory of the fused and unfused forward over "
+                         "a range of sequence lengths, written as a table to OUT_MD")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -223,6 +298,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the forward shards over heads with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
+
+    if args.memory:
+        memory_comparison(args.memory, "python3 bench.py --memory " + args.memory)
+        return
 
     threads = str(len(os.sched_getaffinity(0)))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
