@@ -12,6 +12,8 @@ Sources (the three pages on IO-aware softmax attention):
   * "Flash Attention (FA1)", section "核心局部状态计算和更新公式推导", steps 1-5:
     the per-tile update of (m_i, l_i, O_i).
   * The same page's tiling section: T_r = ceil(N/B_r), T_c = ceil(N/B_c).
+  * The same update (steps 2 and 4-5) applied to whole key chunks: the merge of
+    partial results of the split over keys (attention_split_fp64).
 
 Every function is pinned by tests that do not re-type its formulas (closed forms,
 invariants, brute force, library special cases); no function here is "parity
@@ -20,6 +22,7 @@ unpinned".
 from .attention import (  # noqa: F401
     attention_fp64,
     attention_online_fp64,
+    attention_split_fp64,
     attention_brute_force,
     attention_unfused_bf16,
 )

@@ -5,9 +5,12 @@ Test infrastructure only (see the package docstring): nothing on the GPU path
 imports this module.
 
 Conventions shared by every function here:
-  * q, k, v are float64 numpy arrays of shape [B, H, N, d] (the bf16 inputs
-    widened exactly); ``scale`` multiplies the scores before the softmax (the
-    pages write softmax(QK^T); the 1/sqrt(d) factor is the caller's choice).
+  * q is a float64 numpy array of shape [B, H, N, d] and k, v of shape
+    [B, H, Nk, d] (the bf16 inputs widened exactly). Nk = N for the square
+    forward; decode-shaped problems have a few query rows against many keys
+    (N << Nk), and every definition below reads the same for them. ``scale``
+    multiplies the scores before the softmax (the pages write softmax(QK^T); the
+    1/sqrt(d) factor is the caller's choice).
   * LSE is the natural-log log-sum-exp of the scaled scores of a row,
     LSE_i = ln sum_j exp(s_ij) = m_i + ln l_i. The pages name this per-row fp32
     output of the forward ("写 O + LSE", ai-reference-codex page, section 4 and
@@ -91,8 +94,8 @@ def attention_online_fp64(q, k, v, scale, bc: int, br: int | None = None,
                           deferred: bool = False, rows=None):
     """Tiled online-softmax attention, the FA1 page's per-tile update (steps 1-5).
 
-    K and V are cut along the sequence into tiles of ``bc`` rows (T_c = ceil(N/bc),
-    the last tile ragged); query rows into blocks of ``br`` (default: all of a
+    K and V are cut along the sequence into tiles of ``bc`` rows (T_c = ceil(Nk/bc)
+    over the Nk key rows, the last tile ragged); query rows into blocks of ``br`` (default: all of a
     head's requested rows at once). For each query block the running state
     (m_i, l_i, O_i) starts at (-inf, 0, 0) and each tile j applies:
       1. m~ = rowmax(S_ij),  P~ = exp(S_ij - m~),  l~ = rowsum(P~)
@@ -118,7 +121,7 @@ def attention_online_fp64(q, k, v, scale, bc: int, br: int | None = None,
             m_i = np.full(nr, -np.inf)
             l_i = np.zeros(nr)
             acc = np.zeros((nr, d))  # O_i (normalised) or N_i (deferred)
-            for c0 in range(0, N, bc):
+            for c0 in range(0, K.shape[0], bc):
                 Kj = K[c0:c0 + bc]
                 Vj = V[c0:c0 + bc]
                 S = scale * (Qi @ Kj.T)
@@ -138,6 +141,32 @@ def attention_online_fp64(q, k, v, scale, bc: int, br: int | None = None,
             o_blk = acc / l_i[:, None] if deferred else acc
             _store(O, LSE, rows, pos[r0:r0 + step], o_blk, m_i + np.log(l_i), B, H, N)
     return O, LSE
+
+
+def attention_split_fp64(q, k, v, scale, chunk: int, rows=None):
+    """Attention with the key range cut into chunks whose results are computed
+    separately and merged afterwards: the split over keys of decode-shaped work.
+
+    Chunk s holds keys [s*chunk, (s+1)*chunk) (the last one ragged). Its partial
+    result is the two-pass definition restricted to those keys: O_s (normalised
+    over the chunk) and LSE_s = m_s + ln l_s. The partials are then merged with
+    the FA1 page's update (derivation steps 2 and 4-5) applied to whole chunks
+    instead of tiles. With l_s e^{m_s - m} = e^{LSE_s - m} for any reference m,
+    the update over all chunks reads
+        m = max_s LSE_s,  L = m + ln sum_s e^{LSE_s - m},  O = sum_s e^{LSE_s - L} O_s,
+    and L is the LSE of the whole row.
+    """
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    Nk = k.shape[2]
+    parts = [attention_fp64(q, k[:, :, c0:c0 + chunk], v[:, :, c0:c0 + chunk], scale, rows=rows)
+             for c0 in range(0, Nk, chunk)]
+    lse_s = np.stack([p[1] for p in parts])  # [S, ...rows]
+    m = lse_s.max(axis=0)
+    lse = m + np.log(np.exp(lse_s - m).sum(axis=0))
+    w = np.exp(lse_s - lse)
+    O = sum(w[s][..., None] * parts[s][0] for s in range(len(parts)))
+    return O, lse
 
 
 def attention_brute_force(q, k, v, scale):

@@ -16,7 +16,7 @@ import torch
 
 import attn_inputs
 from oracle import (attention_brute_force, attention_fp64, attention_online_fp64,
-                    attention_unfused_bf16)
+                    attention_split_fp64, attention_unfused_bf16)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_form_cases.json")
 TOL = 1e-12
@@ -141,8 +141,34 @@ def check_library(impl):
     np.testing.assert_allclose(O, torch.matmul(torch.softmax(s, dim=-1), tv).numpy(), atol=TOL)
 
 
+def check_few_queries_many_keys(impl):
+    """Decode shapes, N query rows against Nk != N keys: Q = 0 gives the mean of
+    all Nk value rows and LSE = ln Nk; brute force and torch's fp64 routines on
+    rectangular inputs."""
+    q, _, _ = rand_qkv(1, 2, 3, 8, seed=41)
+    _, k, v = rand_qkv(1, 2, 50, 8, seed=42)
+    O, L = impl(np.zeros_like(q), k, v, 0.35)
+    np.testing.assert_allclose(O, np.broadcast_to(v.mean(axis=2, keepdims=True), O.shape), atol=TOL)
+    np.testing.assert_allclose(L, np.full(L.shape, math.log(50)), atol=TOL)
+    for nq, nk, seed in ((2, 11, 43), (5, 1, 44), (1, 16, 45)):
+        q, _, _ = rand_qkv(1, 1, nq, 4, seed=seed)
+        _, k, v = rand_qkv(1, 1, nk, 4, seed=seed + 100, sigma=2.0)
+        O, L = impl(q, k, v, 0.5)
+        Ob, Lb = attention_brute_force(q[0, 0], k[0, 0], v[0, 0], 0.5)
+        np.testing.assert_allclose(O[0, 0], np.array(Ob), atol=TOL)
+        np.testing.assert_allclose(L[0, 0], np.array(Lb), atol=TOL)
+    q, _, _ = rand_qkv(2, 2, 4, 16, seed=46)
+    _, k, v = rand_qkv(2, 2, 300, 16, seed=47, sigma=2.5)
+    O, L = impl(q, k, v, 0.25)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    s = 0.25 * torch.matmul(tq, tk.transpose(-1, -2).contiguous())
+    np.testing.assert_allclose(L, torch.logsumexp(s, dim=-1).numpy(), atol=TOL)
+    np.testing.assert_allclose(O, torch.matmul(torch.softmax(s, dim=-1), tv).numpy(), atol=TOL)
+
+
 PINS = [check_golden, check_q_zero, check_scale_zero, check_v_constant, check_single_key,
-        check_identity_values, check_permutation, check_brute_force, check_bounds, check_library]
+        check_identity_values, check_permutation, check_brute_force, check_bounds, check_library,
+        check_few_queries_many_keys]
 
 
 def failing_pins(impl):
@@ -172,7 +198,15 @@ def online_deferred_5_br3(q, k, v, scale):
     return attention_online_fp64(q, k, v, scale, bc=5, br=3, deferred=True)
 
 
-@pytest.mark.parametrize("impl", [two_pass, online_normalised_7, online_deferred_5_br3])
+def split_7(q, k, v, scale):
+    return attention_split_fp64(q, k, v, scale, chunk=7)
+
+
+def split_64(q, k, v, scale):
+    return attention_split_fp64(q, k, v, scale, chunk=64)
+
+
+@pytest.mark.parametrize("impl", [two_pass, online_normalised_7, online_deferred_5_br3, split_7, split_64])
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
 def test_oracle_pin(impl, pin):
     pin(impl)
@@ -205,6 +239,29 @@ def test_online_ascending_scores_rescale_every_tile():
         O2, L2 = attention_online_fp64(q, k, v, 0.5, bc=16, deferred=deferred)
         np.testing.assert_allclose(O2, O1, atol=TOL, rtol=0)
         np.testing.assert_allclose(L2, L1, atol=TOL, rtol=0)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 256, 1000, 5000])
+@pytest.mark.parametrize("sigma", [1.0, 2.5])
+def test_split_equals_two_pass(chunk, sigma):
+    """The merged split (decode shape: 4 queries, 1000 keys) reproduces the
+    two-pass result for any chunk size, including one chunk and chunks of one key."""
+    q, _, _ = rand_qkv(2, 2, 4, 16, seed=51, sigma=sigma)
+    _, k, v = rand_qkv(2, 2, 1000, 16, seed=52, sigma=sigma)
+    O1, L1 = attention_fp64(q, k, v, 0.25)
+    O2, L2 = attention_split_fp64(q, k, v, 0.25, chunk=chunk)
+    np.testing.assert_allclose(O2, O1, atol=TOL, rtol=0)
+    np.testing.assert_allclose(L2, L1, atol=TOL, rtol=0)
+
+
+def test_split_rows_subset():
+    q, _, _ = rand_qkv(2, 3, 6, 8, seed=53)
+    _, k, v = rand_qkv(2, 3, 90, 8, seed=54)
+    rows = attn_inputs.sample_rows(2, 3, 6, 10, seed=2)
+    O, L = attention_fp64(q, k, v, 0.3, rows=rows)
+    Os, Ls = attention_split_fp64(q, k, v, 0.3, chunk=16, rows=rows)
+    np.testing.assert_allclose(Os, O, atol=TOL)
+    np.testing.assert_allclose(Ls, L, atol=TOL)
 
 
 def test_rows_subset_matches_full():
@@ -320,6 +377,25 @@ def _mut_online(kind):
     return impl
 
 
+def _mut_split(kind, chunk=4):
+    """Copies of the split-and-merge with one plausible mistake in the merge."""
+    def impl(q, k, v, scale):
+        Nk = k.shape[2]
+        stop = (Nk // chunk) * chunk if kind == "drop_ragged_chunk" and Nk >= chunk else Nk
+        parts = [attention_fp64(q, k[:, :, c0:c0 + chunk], v[:, :, c0:c0 + chunk], scale)
+                 for c0 in range(0, stop, chunk)]
+        lse_s = np.stack([p[1] for p in parts])
+        m = lse_s.max(axis=0)
+        lse = m if kind == "lse_max_only" else m + np.log(np.exp(lse_s - m).sum(axis=0))
+        if kind == "equal_weights":
+            w = np.full(lse_s.shape, 1.0 / len(parts))
+        else:
+            w = np.exp(lse_s - (m + np.log(np.exp(lse_s - m).sum(axis=0))))
+        O = sum(w[s][..., None] * parts[s][0] for s in range(len(parts)))
+        return O, lse
+    return impl
+
+
 MUTANTS = {
     "dropped_scale": _mut_two_pass(score_fn=lambda q, k, s: q @ k.T),
     "sign_flipped_scores": _mut_two_pass(score_fn=lambda q, k, s: -s * q @ k.T),
@@ -333,6 +409,9 @@ MUTANTS = {
     "online_rescale_sign": _mut_online("rescale_sign"),
     "online_forget_l_factor": _mut_online("forget_l_factor"),
     "online_drop_ragged_tile": _mut_online("drop_ragged_tile"),
+    "split_equal_weights": _mut_split("equal_weights"),
+    "split_lse_max_only": _mut_split("lse_max_only"),
+    "split_drop_ragged_chunk": _mut_split("drop_ragged_chunk"),
     "transposed_v_square": lambda q, k, v, s: (attention_fp64(q, k, np.swapaxes(v, -1, -2).copy(), s)
                                                if v.shape[-1] == v.shape[-2] else
                                                (_ for _ in ()).throw(ValueError("shape"))),
