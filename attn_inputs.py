@@ -79,6 +79,74 @@ def make_workload(w: Workload):
     return make_qkv(w.B, w.H, w.N, w.d, w.seed, w.sigma_qk, w.sigma_v)
 
 
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Decode shape: Nq query rows per head against Nk key/value rows."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    seed: int
+    sigma_qk: float = 1.0
+    sigma_v: float = 1.0
+    check_heads: int = 0  # 0: check every head; else this many sampled (b, h) heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def flops(self) -> float:
+        return 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+
+    @property
+    def min_hbm_bytes(self) -> int:
+        """Read Q, K, V once; write O (bf16) and LSE (fp32) once."""
+        return self.B * self.H * (4 * self.Nk * self.d + self.Nq * (4 * self.d + 4))
+
+
+# Decode workloads: a batch of sequences each adding one token (or a few) against
+# its cached keys and values. The first is the benchmark shape (16 sequences at 8K
+# context with the heads and head size of the prefill benchmark); the second one
+# long sequence; the others vary Nq, d, a ragged Nk and a wide score range.
+DECODE_WORKLOADS = (
+    DecodeWorkload("dec_b16h32_q1_k8192_d128", 16, 32, 1, 8192, 128, seed=100, check_heads=24),
+    DecodeWorkload("dec_b1h32_q1_k131072_d128", 1, 32, 1, 131072, 128, seed=101, check_heads=6),
+    DecodeWorkload("dec_b4h16_q4_k4096_d64", 4, 16, 4, 4096, 64, seed=102),
+    DecodeWorkload("dec_b2h8_q16_k30001_d128_wide", 2, 8, 16, 30001, 128, seed=103, sigma_qk=2.5),
+)
+DECODE_BY_NAME = {w.name: w for w in DECODE_WORKLOADS}
+DECODE_HEADLINE = DECODE_WORKLOADS[0]
+
+
+def make_decode_qkv(B: int, H: int, Nq: int, Nk: int, d: int, seed: int, sigma_qk: float = 1.0,
+                    sigma_v: float = 1.0):
+    """Return q [B,H,Nq,d] and k, v [B,H,Nk,d] as contiguous CPU bfloat16 tensors,
+    drawn Q, K, V in that order from one generator seeded with ``seed``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q = (torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32) * sigma_qk).to(torch.bfloat16)
+    k = (torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32) * sigma_qk).to(torch.bfloat16)
+    v = (torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32) * sigma_v).to(torch.bfloat16)
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def make_decode_workload(w: DecodeWorkload):
+    return make_decode_qkv(w.B, w.H, w.Nq, w.Nk, w.d, w.seed, w.sigma_qk, w.sigma_v)
+
+
+def sample_heads(B: int, H: int, count: int, seed: int) -> list:
+    """Sorted distinct (b, h) pairs, the first and the last head always included."""
+    total = B * H
+    if count <= 0 or count >= total:
+        return [(i // H, i % H) for i in range(total)]
+    rng = np.random.default_rng(seed)
+    picks = set(rng.choice(total, size=count, replace=False).tolist()) | {0, total - 1}
+    return [(i // H, i % H) for i in sorted(picks)]
+
+
 def sample_rows(B: int, H: int, N: int, count: int, seed: int) -> np.ndarray:
     """Sorted distinct flat row indices (b*H + h)*N + i, first and last included."""
     total = B * H * N

@@ -7,6 +7,7 @@ in HBM before the timed region. Prints ONE JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--unfused] [--launches-only]
   python bench.py --memory OUT_MD      (peak device memory, fused vs unfused)
+  python bench.py --decode [--workload dec_...]   (decode-shaped forward, GB/s)
 
 The roofline entry is measured live: per-launch HIP events recorded on the stream
 the kernel runs on, averaged over the timed region. Its ``traffic`` field comes
@@ -21,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,6 +34,9 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fwd attention TFLOP/s & % of bf16 MFMA peak, B=1 H=32 N=8192 d=128"
 KERNEL_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_fwd.hip")
 UNFUSED_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_unfused.hip")
+DECODE_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_decode.hip")
+DECODE_METRIC = "decode attention GB/s (Q, K, V read and O, LSE written once) & % of HBM peak, " \
+                "B=16 H=32 Nq=1 Nk=8192 d=128"
 
 
 def kernel_source_hash(path: str = KERNEL_SRC) -> str:
@@ -39,14 +44,14 @@ def kernel_source_hash(path: str = KERNEL_SRC) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, stem: str = "fa_fwd", src: str = KERNEL_SRC):
     """HBM bytes per launch from the committed counter summary, if still current."""
-    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -98,13 +103,19 @@ def _read_counter_csv(path):
 UNFUSED_KERNELS = ("unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel")
 
 
-def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False):
+DECODE_KERNELS = ("dec_split_kernel", "dec_merge_kernel")
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, decode=False):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel (or of the
-    three unfused kernels, summed per launch) by what the same counters read for the
-    plain copy of ``copy_bytes`` bytes in the same run."""
+    three unfused kernels, or of the two decode kernels, summed per launch) by what
+    the same counters read for the plain copy of ``copy_bytes`` bytes in the same run."""
     import attn_inputs
 
-    w = attn_inputs.HEADLINE if workload is None else attn_inputs.WORKLOAD_BY_NAME[workload]
+    if decode:
+        w = attn_inputs.DECODE_HEADLINE if workload is None else attn_inputs.DECODE_BY_NAME[workload]
+    else:
+        w = attn_inputs.HEADLINE if workload is None else attn_inputs.WORKLOAD_BY_NAME[workload]
     fetch = _read_counter_csv(fetch_csv)
     write = _read_counter_csv(write_csv)
 
@@ -116,7 +127,7 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False):
 
     def per_launch(table, counter):
         """Average KiB per launch: one kernel (fused) or the sum of the three."""
-        names = UNFUSED_KERNELS if unfused else ("fa_fwd_kernel",)
+        names = DECODE_KERNELS if decode else UNFUSED_KERNELS if unfused else ("fa_fwd_kernel",)
         total, raw = 0.0, []
         for name in names:
             vals = pick(table, counter, lambda k, n=name: n in k)
@@ -125,7 +136,7 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False):
         per = [round(sum(r[i] for r in raw), 1) for i in range(min(len(r) for r in raw))]
         return total, per
 
-    is_copy = lambda k: "fa_fwd_kernel" not in k and "unf_" not in k
+    is_copy = lambda k: "fa_fwd_kernel" not in k and "unf_" not in k and "dec_" not in k
     copy_fetch = pick(fetch, "FETCH_SIZE", is_copy)[0] * 1024.0
     copy_write = pick(write, "WRITE_SIZE", is_copy)[0] * 1024.0
     f_scale = copy_bytes / copy_fetch
@@ -136,8 +147,9 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False):
     write_b = fa_write_kib * 1024.0 * w_scale
     rec = {
         "workload": w.name,
-        "path": "unfused-3-kernel" if unfused else "fused",
-        "kernel_source_sha256_16": kernel_source_hash(UNFUSED_SRC if unfused else KERNEL_SRC),
+        "path": "decode split+merge" if decode else "unfused-3-kernel" if unfused else "fused",
+        "kernel_source_sha256_16": kernel_source_hash(DECODE_SRC if decode else UNFUSED_SRC if unfused
+                                                      else KERNEL_SRC),
         "hbm_bytes_per_launch": round(fetch_b + write_b),
         "fetch_bytes_per_launch": round(fetch_b),
         "write_bytes_per_launch": round(write_b),
@@ -149,7 +161,7 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False):
         "fetch_kib_raw_per_launch": fa_fetch,
         "write_kib_raw_per_launch": fa_write,
     }
-    stem = "fa_unfused" if unfused else "fa_fwd"
+    stem = "fa_decode" if decode else "fa_unfused" if unfused else "fa_fwd"
     path = os.path.join(ROOT, "profiles", f"{stem}_{w.name}_traffic.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -163,19 +175,29 @@ def summarize_trace(stats_csv, command, workload):
 
     import attn_inputs
 
-    w = attn_inputs.HEADLINE if workload is None else attn_inputs.WORKLOAD_BY_NAME[workload]
     rows = list(csv.DictReader(open(stats_csv)))
     fused = any("fa_fwd_kernel" in r["Name"] for r in rows)
-    lines = [f"# Kernel durations, workload {w.name} (B={w.B} H={w.H} N={w.N} d={w.d})", "",
+    decode = any("dec_split_kernel" in r["Name"] for r in rows)
+    if decode:
+        w = attn_inputs.DECODE_HEADLINE if workload is None else attn_inputs.DECODE_BY_NAME[workload]
+        shape = f"B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d}"
+    else:
+        w = attn_inputs.HEADLINE if workload is None else attn_inputs.WORKLOAD_BY_NAME[workload]
+        shape = f"B={w.B} H={w.H} N={w.N} d={w.d}"
+    lines = [f"# Kernel durations, workload {w.name} ({shape})", "",
              "Command, run from the repository root with TMPDIR=/tmp:", "", "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | stddev us |", "|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
         short = name[:60]
-        for base in ("fa_fwd_kernel", "unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel"):
+        for base in ("fa_fwd_kernel", "unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel") + DECODE_KERNELS:
             if base in name:
-                dim = next((dd for dd in ("128", "64") if f"<{dd}>" in name or f"ILi{dd}E" in name), None)
-                short = f"{base}<{dim}>" if dim else base
+                args = re.findall(r"ILi(\d+)E(?:Li(\d+)E)?", name)
+                if args:
+                    short = f"{base}<{','.join(x for x in args[0] if x)}>"
+                else:
+                    dim = next((dd for dd in ("128", "64") if f"<{dd}>" in name), None)
+                    short = f"{base}<{dim}>" if dim else base
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['StdDev']) / 1e3:.1f} |")
     if fused:
@@ -185,10 +207,118 @@ def summarize_trace(stats_csv, command, workload):
         lines += ["", f"Fused kernel at its average duration: {w.flops:.4e} FLOP per launch -> {tf:.1f} TFLOP/s, "
                       f"{tf / MFMA_BF16_PEAK_TFLOPS:.4f} of the {MFMA_BF16_PEAK_TFLOPS} TFLOP/s bf16 MFMA peak.",
                   f"Kernel source sha256[:16] of fa_fwd.hip: {kernel_source_hash()}."]
-    path = os.path.join(ROOT, "profiles", f"{'fa_fwd' if fused else 'fa_unfused'}_{w.name}_kernel_trace.md")
+    if decode:
+        split = [r for r in rows if any(kname in r["Name"] for kname in DECODE_KERNELS)]
+        total_s = sum(float(r["AverageNs"]) for r in split) * 1e-9
+        gbs = w.min_hbm_bytes / total_s / 1e9
+        lines += ["", f"Decode kernels (split + merge) at their average durations: {w.min_hbm_bytes} algorithmic "
+                      f"HBM bytes per call -> {gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.4f} of the {HBM_PEAK_GBS:.0f} GB/s "
+                      f"HBM peak.",
+                  f"Kernel source sha256[:16] of fa_decode.hip: {kernel_source_hash(DECODE_SRC)}."]
+    stem = "fa_fwd" if fused else "fa_decode" if decode else "fa_unfused"
+    path = os.path.join(ROOT, "profiles", f"{stem}_{w.name}_kernel_trace.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def decode_cpu_baseline(w, q, k, v, target_s: float = 10.0):
+    """The fp64 oracle on whole heads of the decode workload until ``target_s`` of CPU
+    work has accumulated; rate in algorithmic GB/s like the GPU figure."""
+    import attn_inputs
+    from oracle import attention_fp64
+
+    heads, t_total = 0, 0.0
+    BH = w.B * w.H
+    while heads < BH and t_total < target_s:
+        b, h = divmod(heads, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        qh, kh, vh = (attn_inputs.bf16_to_f64(t[sl]) for t in (q, k, v))
+        t0 = time.perf_counter()
+        attention_fp64(qh, kh, vh, w.scale)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    per_head = w.min_hbm_bytes / BH
+    return {
+        "value": heads * per_head / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"{heads} of {BH} heads (all {w.Nq} query rows against {w.Nk} keys each), fp64 numpy "
+                  f"two-pass oracle, {t_total:.1f} s",
+    }
+
+
+def decode_bench(args):
+    """Time the decode-shaped forward (split + merge kernels) and print one JSON line."""
+    import torch
+
+    import attn_inputs
+    import io_aware_softmax_attn_amd as fa
+
+    w = attn_inputs.DECODE_HEADLINE if args.workload is None else attn_inputs.DECODE_BY_NAME[args.workload]
+    q, k, v = attn_inputs.make_decode_workload(w)
+    dev = torch.device("cuda:0")
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qg)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    splits, chunk, ws_bytes = fa.fa_decode_plan(w.B, w.H, w.Nq, w.Nk, w.d)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    # K and V of the benchmark shape (2.1 GB) exceed the 256 MB Infinity Cache many
+    # times over, so back-to-back calls cannot serve each other from cache.
+    for _ in range(args.warmup):
+        fa.fa_decode_fwd(qg, kg, vg, o, lse, ws, scale=w.scale, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        fa.fa_decode_fwd(qg, kg, vg, o, lse, ws, scale=w.scale, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg_ms = sum(per_ms) / len(per_ms)
+    gbs = w.min_hbm_bytes / (avg_ms * 1e-3) / 1e9
+    line = {
+        "metric": DECODE_METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(max(wall * 1e3 / args.steps, avg_ms), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "splits": splits, "chunk": chunk, "path": "decode split+merge"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(w.name, "fa_decode", DECODE_SRC),
+            "kernel_ms_avg": round(avg_ms, 4),
+            "kernel_ms_min": round(min(per_ms), 4),
+            "min_hbm_bytes_per_launch": w.min_hbm_bytes,
+            "tflops": round(w.flops / (avg_ms * 1e-3) / 1e12, 2),
+        },
+    }
+    if not args.launches_only and not args.no_cpu_baseline:
+        line["cpu_baseline"] = decode_cpu_baseline(w, q, k, v)
+    print(json.dumps(line), flush=True)
 
 
 # Shapes of the device-memory comparison: (B, H, d, sequence lengths).
@@ -281,6 +411,9 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="no GPU work: turn a rocprofv3 --kernel-trace --stats kernel_stats.csv into "
                          "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin")
+    ap.add_argument("--decode", action="store_true",
+                    help="the decode-shaped forward (few queries against many keys) instead of the prefill "
+                         "benchmark; also selects the decode kernels for --summarize-pmc")
     ap.add_argument("--memory", metavar="OUT_MD",
                     help="instead of timing: peak device memory of the fused and unfused forward over "
                          "a range of sequence lengths, written as a table to OUT_MD")
@@ -288,7 +421,7 @@ def main():
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_calibration,
-                      unfused=args.unfused)
+                      unfused=args.unfused, decode=args.decode)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload)
@@ -306,6 +439,10 @@ def main():
     threads = str(len(os.sched_getaffinity(0)))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ.setdefault(var, threads)
+
+    if args.decode:
+        decode_bench(args)
+        return
 
     import torch
 

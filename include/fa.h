@@ -47,13 +47,13 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL */
-  FA_ERR_SHAPE = -2,     /* B, H or N negative */
+  FA_ERR_SHAPE = -2,     /* B, H or N negative; decode: Nq or Nk out of range */
   FA_ERR_HEADDIM = -3,   /* d not in {64, 128} */
   FA_ERR_ALIGN = -4,     /* a pointer is not aligned as stated above */
   FA_ERR_SCALE = -5,     /* scale not finite or negative */
   FA_ERR_ALIAS = -6,     /* O or LSE overlaps an input or each other */
   FA_ERR_OVERFLOW = -7,  /* sizes overflow 64-bit byte counts or the launch grid */
-  FA_ERR_WORKSPACE = -8, /* unfused workspace missing or too small */
+  FA_ERR_WORKSPACE = -8, /* workspace missing, too small, misaligned or overlapping */
   FA_ERR_HIP = -9,       /* the HIP runtime reported an error */
   FA_ERR_DEVICE = -10    /* the current device is not gfx950 */
 } fa_status;
@@ -103,6 +103,46 @@ int fa_select_blocks(int d, int N, int B, int H, int* br, int* bc, int* nwaves);
 int fa_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse,
                   int B, int H, int N, int d, float scale,
                   int need_workspace, const void* workspace, size_t workspace_bytes);
+
+/*
+ * Decode-shaped forward: Nq query rows per head (1 <= Nq <= FA_DECODE_MAX_NQ)
+ * against Nk keys (1 <= Nk <= FA_DECODE_MAX_NK), the workload the KP page
+ * contrasts with prefill ("FlashAttention：IO 感知的精确注意力", sections 常见误区
+ * and 自测题: decode is limited by memory traffic). q, o: bf16 [B,H,Nq,d];
+ * k, v: bf16 [B,H,Nk,d]; lse: fp32 [B,H,Nq]. Same definition as fa_fwd, with
+ * j running over the Nk keys: o[i] = sum_j p_ij v[j] / sum_j p_ij and
+ * lse[i] = ln sum_j exp(s_ij). Same conventions as above (d in {64, 128},
+ * alignment, no overlap of o and lse with anything, asynchronous on stream),
+ * plus a caller-owned device workspace of at least the bytes fa_decode_plan
+ * reports, 16-byte aligned and overlapping no tensor argument.
+ *
+ * Two kernels: the first splits each head's keys into chunks, one workgroup per
+ * chunk, and writes each chunk's normalised partial O and its LSE (fp32) to the
+ * workspace; the second merges the partials of each row with the FA1 page's
+ * update (derivation steps 2 and 4-5) applied to whole chunks. Scores and
+ * probabilities stay in fp32 (bf16 products accumulate exactly in fp32); O is
+ * rounded to bf16 (nearest-even) once, at the end. When B*H*Nq == 0 the call is
+ * a no-op. Deterministic for a given shape: the split depends on the shape only.
+ */
+#define FA_DECODE_MAX_NQ 16
+#define FA_DECODE_MAX_NK (1 << 30)
+int fa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int d, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The key split fa_decode_fwd uses for this shape: *splits chunks of *chunk keys
+ * per (b, h) (the last chunk may be shorter), and the workspace it needs,
+ * B*H*splits*Nq*(d+1)*4 bytes rounded up to 256 (partial O, then partial LSE).
+ * Any output pointer may be NULL. Returns FA_OK, FA_ERR_SHAPE, FA_ERR_HEADDIM or
+ * FA_ERR_OVERFLOW (then *workspace_bytes is 0). Pure host code.
+ */
+int fa_decode_plan(int B, int H, int Nq, int Nk, int d, int* splits, int* chunk, size_t* workspace_bytes);
+
+/* Argument validation of fa_decode_fwd, without a GPU. Pure host code. */
+int fa_decode_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                         int B, int H, int Nq, int Nk, int d, float scale,
+                         const void* workspace, size_t workspace_bytes);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);

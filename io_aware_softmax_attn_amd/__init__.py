@@ -20,8 +20,11 @@ from . import build as _build
 __all__ = [
     "FaError", "lib", "fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks",
     "fa_check_args", "fa_status_string", "fa_version", "forward", "unfused_forward",
+    "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args", "decode_forward", "DECODE_MAX_NQ",
     "STATUS",
 ]
+
+DECODE_MAX_NQ = 16  # FA_DECODE_MAX_NQ
 
 STATUS = {
     "FA_OK": 0, "FA_ERR_NULL": -1, "FA_ERR_SHAPE": -2, "FA_ERR_HEADDIM": -3, "FA_ERR_ALIGN": -4,
@@ -58,6 +61,12 @@ def _load() -> ctypes.CDLL:
     dll.fa_select_blocks.restype = i
     dll.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz]
     dll.fa_check_args.restype = i
+    dll.fa_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp]
+    dll.fa_decode_fwd.restype = i
+    dll.fa_decode_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(sz)]
+    dll.fa_decode_plan.restype = i
+    dll.fa_decode_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz]
+    dll.fa_decode_check_args.restype = i
     dll.fa_status_string.argtypes = [i]
     dll.fa_status_string.restype = ctypes.c_char_p
     dll.fa_version.argtypes = []
@@ -117,7 +126,7 @@ def _stream_handle(stream, device) -> int | None:
     return int(stream)
 
 
-def _shape_of(q, k, v, o, lse):
+def _check_tensors(q, k, v, o, lse):
     for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
                         ("o", o, torch.bfloat16), ("lse", lse, torch.float32)):
         if not isinstance(t, torch.Tensor):
@@ -130,6 +139,10 @@ def _shape_of(q, k, v, o, lse):
             raise ValueError(f"{name} must be contiguous")
     if len({t.device for t in (q, k, v, o, lse)}) != 1:
         raise ValueError("q, k, v, o and lse must be on the same GPU")
+
+
+def _shape_of(q, k, v, o, lse):
+    _check_tensors(q, k, v, o, lse)
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or o.shape != q.shape:
         raise ValueError("q, k, v, o must all have shape [B, H, N, d]")
     if tuple(lse.shape) != tuple(q.shape[:3]):
@@ -181,3 +194,57 @@ def unfused_forward(q, k, v, scale=None, stream=None):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     ws = torch.empty(max(fa_unfused_workspace_bytes(B, H, N), 256), dtype=torch.uint8, device=q.device)
     return fa_unfused_fwd(q, k, v, o, lse, ws, scale=scale, stream=stream)
+
+
+def fa_decode_plan(B: int, H: int, Nq: int, Nk: int, d: int):
+    """(splits, chunk, workspace_bytes) that fa_decode_fwd uses for this shape."""
+    sp, ch, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    _raise(lib.fa_decode_plan(int(B), int(H), int(Nq), int(Nk), int(d), ctypes.byref(sp), ctypes.byref(ch),
+                              ctypes.byref(ws)), "fa_decode_plan")
+    return sp.value, ch.value, ws.value
+
+
+def fa_decode_check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, workspace=None, workspace_bytes=0) -> int:
+    """Raw pointer-level validation of fa_decode_fwd (integers or None); returns the status code."""
+    return lib.fa_decode_check_args(q, k, v, o, lse, int(B), int(H), int(Nq), int(Nk), int(d), float(scale),
+                                    workspace, int(workspace_bytes))
+
+
+def _decode_shape_of(q, k, v, o, lse):
+    _check_tensors(q, k, v, o, lse)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("q, o must have shape [B, H, Nq, d] and k, v shape [B, H, Nk, d]")
+    if k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("q and k must agree in B, H and d")
+    if tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must have shape [B, H, Nq]")
+    B, H, Nq, d = (int(x) for x in q.shape)
+    return B, H, Nq, int(k.shape[2]), d
+
+
+def fa_decode_fwd(q, k, v, o, lse, workspace, scale=None, stream=None):
+    """Decode-shaped forward (Nq <= 16 query rows against Nk keys) into caller-provided
+    ``o`` and ``lse``, with ``workspace`` a uint8 GPU tensor of at least the bytes
+    fa_decode_plan reports."""
+    B, H, Nq, Nk, d = _decode_shape_of(q, k, v, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    if workspace.device != q.device:
+        raise ValueError("workspace must be on the same GPU as the tensors")
+    nbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _raise(lib.fa_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                                 _ptr(workspace), nbytes, _stream_handle(stream, q.device)), "fa_decode_fwd")
+    return o, lse
+
+
+def decode_forward(q, k, v, scale=None, stream=None):
+    """Allocate O, LSE and the workspace and run :func:`fa_decode_fwd`. Returns (o, lse)."""
+    B, H, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _, _, ws_bytes = fa_decode_plan(B, H, Nq, k.shape[2], d)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    return fa_decode_fwd(q, k, v, o, lse, ws, scale=scale, stream=stream)

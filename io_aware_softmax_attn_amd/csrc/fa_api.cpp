@@ -35,13 +35,13 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "B, H and N must be >= 0";
+    case FA_ERR_SHAPE: return "B, H and N must be >= 0 (decode: 1 <= Nq <= 16 and 1 <= Nk <= 2^30)";
     case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
     case FA_ERR_ALIGN: return "q, k, v, o and workspace must be 16-byte aligned, lse 4-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
     case FA_ERR_ALIAS: return "o or lse overlaps an input, or each other";
     case FA_ERR_OVERFLOW: return "problem size overflows 64-bit byte counts or the launch grid";
-    case FA_ERR_WORKSPACE: return "unfused workspace is missing, too small, misaligned or overlaps a tensor";
+    case FA_ERR_WORKSPACE: return "workspace is missing, too small, misaligned or overlaps a tensor";
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
     default: return "unknown status";
@@ -105,6 +105,72 @@ int fa_check_args(const void* q, const void* k, const void* v, const void* o, co
       return FA_ERR_WORKSPACE;
   }
   return FA_OK;
+}
+
+int fa_decode_plan(int B, int H, int Nq, int Nk, int d, int* splits, int* chunk, size_t* workspace_bytes) {
+  if (workspace_bytes) *workspace_bytes = 0;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || Nq > FA_DECODE_MAX_NQ || Nk > FA_DECODE_MAX_NK) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if ((uint64_t)B * (uint64_t)H > (std::numeric_limits<uint64_t>::max() >> 31)) return FA_ERR_OVERFLOW;
+  const fa::DecodePlan p = fa::decode_plan(B, H, Nq, Nk, d);
+  uint64_t groups, rows, floats, bytes;
+  if (!mul_ok((uint64_t)B * (uint64_t)H, (uint64_t)p.splits, &groups) || !mul_ok(groups, (uint64_t)Nq, &rows) ||
+      !mul_ok(rows, (uint64_t)d + 1, &floats) || !mul_ok(floats, 4, &bytes) ||
+      bytes > std::numeric_limits<uint64_t>::max() - 255)
+    return FA_ERR_OVERFLOW;
+  bytes = (bytes + 255) & ~uint64_t(255);
+  if (bytes > std::numeric_limits<size_t>::max()) return FA_ERR_OVERFLOW;
+  if (splits) *splits = p.splits;
+  if (chunk) *chunk = p.chunk;
+  if (workspace_bytes) *workspace_bytes = (size_t)bytes;
+  return FA_OK;
+}
+
+int fa_decode_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
+                         int Nq, int Nk, int d, float scale, const void* workspace, size_t workspace_bytes) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!std::isfinite(scale) || scale < 0.0f) return FA_ERR_SCALE;
+  if ((uint64_t)B * (uint64_t)H > (std::numeric_limits<uint64_t>::max() >> 31)) return FA_ERR_OVERFLOW;
+  const uint64_t bh = (uint64_t)B * (uint64_t)H;
+  const uint64_t rows64 = bh * (uint64_t)Nq;
+  if (rows64 == 0) return FA_OK;  // empty problem: nothing is touched
+  if (Nq > FA_DECODE_MAX_NQ || Nk < 1 || Nk > FA_DECODE_MAX_NK) return FA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int splits = 0;
+  size_t need = 0;
+  const int pst = fa_decode_plan(B, H, Nq, Nk, d, &splits, nullptr, &need);
+  if (pst != FA_OK) return pst;
+  uint64_t qb, kb, lb, groups;
+  if (!mul_ok(rows64 * (uint64_t)d, 2, &qb) || !mul_ok(bh * (uint64_t)Nk, (uint64_t)d * 2, &kb) ||
+      !mul_ok(rows64, 4, &lb) || !mul_ok(bh, (uint64_t)splits, &groups))
+    return FA_ERR_OVERFLOW;
+  // Launch grids: B*H*splits split workgroups, B*H*Nq merge rows.
+  if (groups > (uint64_t)std::numeric_limits<int32_t>::max() || rows64 > (uint64_t)std::numeric_limits<int32_t>::max())
+    return FA_ERR_OVERFLOW;
+  auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
+    return FA_ERR_ALIGN;
+  const size_t qs = (size_t)qb, ks = (size_t)kb, ls = (size_t)lb;
+  if (overlaps(o, qs, q, qs) || overlaps(o, qs, k, ks) || overlaps(o, qs, v, ks) || overlaps(lse, ls, q, qs) ||
+      overlaps(lse, ls, k, ks) || overlaps(lse, ls, v, ks) || overlaps(lse, ls, o, qs))
+    return FA_ERR_ALIAS;
+  if (!workspace || workspace_bytes < need || misaligned(workspace, 16)) return FA_ERR_WORKSPACE;
+  if (overlaps(workspace, need, q, qs) || overlaps(workspace, need, k, ks) || overlaps(workspace, need, v, ks) ||
+      overlaps(workspace, need, o, qs) || overlaps(workspace, need, lse, ls))
+    return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+int fa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+                  float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = fa_decode_check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)Nq == 0) return FA_OK;
+  const int dev = fa::device_is_gfx950();
+  if (dev < 0) return dev;
+  if (dev == 0) return FA_ERR_DEVICE;
+  return fa::launch_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, workspace, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, float scale,

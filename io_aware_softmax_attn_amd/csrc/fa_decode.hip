@@ -1,0 +1,339 @@
+// Decode-shaped attention forward on gfx950: a few query rows per head (Nq <= 16)
+// against a long key/value sequence (Nk keys), the workload the KP page contrasts
+// with prefill (sections 常见误区 and 自测题: decode is bound by memory traffic,
+// not by arithmetic). Per key the work is 4*Nq*d flops against 4*d bytes of K and
+// V, at most 16 flops per byte, far below the matrix cores' ridge, so this path is
+// written for HBM bandwidth: coalesced 16-byte row loads, dot products and the
+// PV sum on the vector ALUs in fp32, and enough independent workgroups in flight.
+//
+// The key range of each (b, h) is split into chunks, one workgroup per chunk
+// (kernel 1), whose partial results are merged afterwards (kernel 2):
+//   kernel 1  per chunk s: O_s = softmax over the chunk's keys applied to V
+//             (fp32, normalised) and LSE_s (log2 units), into the workspace;
+//   kernel 2  per query row: the FA1 page's update (derivation steps 2 and 4-5)
+//             over whole chunks, m = max_s LSE_s,
+//             L = m + log2 sum_s 2^(LSE_s - m),  O = sum_s 2^(LSE_s - L) O_s,
+//             then O to bf16 (nearest-even) and LSE = ln2 * L.
+// Inside a chunk each wave runs the online softmax (same page, steps 1-5) over
+// batches of keys; the waves' states are merged through LDS at the end.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Lane layout of one wave's row loads: a K or V row of D bf16 is kLanesPerKey
+// 16-byte pieces, so one 64-lane load covers kGroups consecutive rows (1 KB at
+// D = 128, fully coalesced); lane l holds piece l % kLanesPerKey of row l / kLanesPerKey.
+template <int D>
+struct DecCfg {
+  static constexpr int kLanesPerKey = D / 8;
+  static constexpr int kGroups = 64 / kLanesPerKey;
+  static constexpr int kLoads = 4;                      // row loads per wave per batch
+  static constexpr int kWaveKeys = kLoads * kGroups;    // keys per wave per batch
+  static constexpr int kBlockKeys = 4 * kWaveKeys;      // keys per workgroup per batch
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the kLanesPerKey lanes of one row (all lanes get the same value: each
+// step adds two partial sums that are equal as a set, and fp32 addition is
+// commutative).
+template <int D>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: pairs
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: quads
+  x += dpp<0x141>(x);  // row_half_mirror: the two quads of each 8 lanes
+  if constexpr (D == 128) x += dpp<0x140>(x);  // row_mirror: the two halves of each 16 lanes
+  return x;
+}
+
+__device__ __forceinline__ f32x2_t swap16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return f32x2_t{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+}
+__device__ __forceinline__ f32x2_t swap32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return f32x2_t{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+}
+
+// Combine the kGroups row groups of a wave: lanes holding the same piece index in
+// different groups. Every lane ends with the same result.
+template <int D>
+__device__ __forceinline__ float groups_sum(float x) {
+  if constexpr (D == 64) x += dpp<0x128>(x);  // row_ror:8, the two 8-lane groups of a row
+  f32x2_t r = swap16(x);
+  x = r[0] + r[1];
+  r = swap32(x);
+  return r[0] + r[1];
+}
+template <int D>
+__device__ __forceinline__ float groups_max(float x) {
+  if constexpr (D == 64) x = fmaxf(x, dpp<0x128>(x));
+  f32x2_t r = swap16(x);
+  x = fmaxf(r[0], r[1]);
+  r = swap32(x);
+  return fmaxf(r[0], r[1]);
+}
+
+// Dot product of 8 bf16 pairs, fp32 accumulation. Each vector element is copied
+// to a scalar before the bit cast: a bit cast applied to an element of an
+// ext_vector_type value directly reads element 0 for every index with this
+// compiler.
+__device__ __forceinline__ float dot8(const u32x4_t& a, const u32x4_t& b) {
+  float d = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const unsigned aj = a[j], bj = b[j];
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aj), __builtin_bit_cast(bf16x2_t, bj), d, false);
+  }
+  return d;
+}
+
+// Kernel 1. Workgroup (bh, s) covers keys [s*chunk, min((s+1)*chunk, Nk)) of head
+// bh for all Nq query rows (NQ >= Nq is the compiled row count; rows >= Nq are
+// zero and never stored). Wave w takes keys base + w*kWaveKeys + u*kGroups + g of
+// each batch; keys past the chunk's end are masked (score -inf), and their loads
+// read row min(key, Nk-1), which is inside the head. Writes part_o[bh][s][i][:]
+// (fp32, normalised over the chunk) and part_lse[bh][s][i] (log2 units).
+template <int D, int NQ>
+__global__ void __launch_bounds__(256) dec_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                        const __bf16* __restrict__ v, float* __restrict__ part_o,
+                                                        float* __restrict__ part_lse, int Nq, int Nk, int chunk,
+                                                        int S, float c) {
+  using C = DecCfg<D>;
+  constexpr int L = C::kLoads;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = lane % C::kLanesPerKey, g = lane / C::kLanesPerKey;
+  const int s = blockIdx.x % S;
+  const size_t bh = blockIdx.x / S;
+  const int k0 = s * chunk;
+  const int k1 = min(k0 + chunk, Nk);
+
+  u32x4_t qv[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    qv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (i < Nq) qv[i] = *(const u32x4_t*)(q + (bh * Nq + i) * D + 8 * t);
+  }
+  float m[NQ], l[NQ], acc[NQ][8];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    m[i] = -__builtin_inff();
+    l[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+  }
+
+  const __bf16* kh = k + bh * (size_t)Nk * D + 8 * t;
+  const __bf16* vh = v + bh * (size_t)Nk * D + 8 * t;
+  const int wkey0 = wave * C::kWaveKeys + g;  // this lane's key offset inside a batch, load 0
+  auto load = [&](int base, u32x4_t (&kr)[L], u32x4_t (&vr)[L]) {
+#pragma unroll
+    for (int u = 0; u < L; ++u) {
+      const size_t row = (size_t)min(base + wkey0 + u * C::kGroups, Nk - 1);
+      kr[u] = __builtin_nontemporal_load((const u32x4_t*)(kh + row * D));
+      vr[u] = __builtin_nontemporal_load((const u32x4_t*)(vh + row * D));
+    }
+  };
+  auto process = [&](int base, const u32x4_t (&kr)[L], const u32x4_t (&vr)[L]) {
+    float sc[L][NQ];
+#pragma unroll
+    for (int u = 0; u < L; ++u) {
+      const bool live = base + wkey0 + u * C::kGroups < k1;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const float d = row_sum<D>(dot8(kr[u], qv[i]));
+        sc[u][i] = live ? d * c : -__builtin_inff();
+      }
+    }
+    float p[L][NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      float bm = sc[0][i];
+#pragma unroll
+      for (int u = 1; u < L; ++u) bm = fmaxf(bm, sc[u][i]);
+      bm = groups_max<D>(bm);
+      const float mn = fmaxf(m[i], bm);
+      const float ms = mn == -__builtin_inff() ? 0.0f : mn;  // no key yet: keep every term at 0
+      const float alpha = __builtin_amdgcn_exp2f(m[i] - ms);
+      m[i] = mn;
+      float ls = l[i] * alpha;
+#pragma unroll
+      for (int u = 0; u < L; ++u) {
+        p[u][i] = __builtin_amdgcn_exp2f(sc[u][i] - ms);
+        ls += p[u][i];
+      }
+      l[i] = ls;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < L; ++u) {
+      float vf[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // bf16 pair -> two fp32 (bf16 is the top half of fp32)
+        const unsigned w = vr[u][j];
+        vf[2 * j] = __builtin_bit_cast(float, w << 16);
+        vf[2 * j + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(p[u][i], vf[j], acc[i][j]);
+      }
+    }
+  };
+
+  // Batches of kBlockKeys keys; the next batch's rows are loaded before the
+  // current one is processed.
+  u32x4_t kc[L], vc[L], kn[L], vn[L];
+  load(k0, kc, vc);
+  for (int base = k0; base < k1; base += C::kBlockKeys) {
+    const bool more = base + C::kBlockKeys < k1;
+    if (more) load(base + C::kBlockKeys, kn, vn);
+    process(base, kc, vc);
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < L; ++u) {
+        kc[u] = kn[u];
+        vc[u] = vn[u];
+      }
+    }
+  }
+
+  // Each group of lanes summed its own keys; the wave's state is the sum over groups
+  // (m is already wave-wide).
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    l[i] = groups_sum<D>(l[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = groups_sum<D>(acc[i][j]);
+  }
+
+  // Merge the four waves' states (m_w, l_w, acc_w) through LDS.
+  __shared__ float sm[4][NQ], sl[4][NQ];
+  __shared__ float so[4][NQ][D];
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      sm[wave][i] = m[i];
+      sl[wave][i] = l[i];
+    }
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) so[wave][i][8 * t + j] = acc[i][j];
+    }
+  }
+  __syncthreads();
+  const size_t out_row0 = (bh * S + s) * (size_t)Nq;
+  for (int e = threadIdx.x; e < Nq * D; e += 256) {
+    const int i = e / D, col = e % D;
+    float mx = sm[0][i];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, sm[w][i]);
+    float den = 0.0f, num = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = __builtin_amdgcn_exp2f(sm[w][i] - mx);  // 0 for a wave that saw no key
+      den = __builtin_fmaf(a, sl[w][i], den);
+      num = __builtin_fmaf(a, so[w][i][col], num);
+    }
+    part_o[(out_row0 + i) * D + col] = num / den;
+    if (col == 0) part_lse[out_row0 + i] = mx + __builtin_log2f(den);
+  }
+}
+
+// Kernel 2: one wave per query row (b, h, i); lane l owns columns D/64*l .. +D/64-1.
+template <int D>
+__global__ void __launch_bounds__(256) dec_merge_kernel(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_lse, __bf16* __restrict__ o,
+                                                        float* __restrict__ lse, int rows, int Nq, int S) {
+  constexpr int kCols = D / 64;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (size_t)rows) return;
+  const int lane = threadIdx.x & 63;
+  const size_t bh = row / Nq;
+  const int i = (int)(row % Nq);
+  const float* pl = part_lse + bh * S * (size_t)Nq + i;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[(size_t)s * Nq]);
+  float den = 0.0f, acc[kCols] = {};
+  for (int s = 0; s < S; ++s) {
+    const float w = __builtin_amdgcn_exp2f(pl[(size_t)s * Nq] - mx);
+    den += w;
+    const float* po = part_o + ((bh * S + s) * Nq + i) * D + kCols * lane;
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) acc[j] = __builtin_fmaf(w, po[j], acc[j]);
+  }
+  const float inv = 1.0f / den;
+  __bf16* orow = o + row * D + kCols * lane;
+  if constexpr (kCols == 2) {
+    *(bf16x2_t*)orow = __builtin_convertvector((f32x2_t){acc[0] * inv, acc[1] * inv}, bf16x2_t);
+  } else {
+    orow[0] = (__bf16)(acc[0] * inv);
+  }
+  if (lane == 0) lse[row] = kLn2 * (mx + __builtin_log2f(den));
+}
+
+template <int D, int NQ>
+void launch_split(const void* q, const void* k, const void* v, float* po, float* pl, int BH, int Nq, int Nk,
+                  const DecodePlan& p, float c, hipStream_t st) {
+  hipLaunchKernelGGL((dec_split_kernel<D, NQ>), dim3((unsigned)(BH * p.splits)), dim3(256), 0, st,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, po, pl, Nq, Nk, p.chunk, p.splits, c);
+}
+
+template <int D>
+void launch_split_d(const void* q, const void* k, const void* v, float* po, float* pl, int BH, int Nq, int Nk,
+                    const DecodePlan& p, float c, hipStream_t st) {
+  if (Nq <= 1) launch_split<D, 1>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
+  else if (Nq <= 2) launch_split<D, 2>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
+  else if (Nq <= 4) launch_split<D, 4>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
+  else if (Nq <= 8) launch_split<D, 8>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
+  else launch_split<D, 16>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
+}
+
+}  // namespace
+
+int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int d, float scale, void* workspace, void* stream) {
+  const DecodePlan p = decode_plan(B, H, Nq, Nk, d);
+  const int BH = B * H;
+  float* po = (float*)workspace;
+  float* pl = po + (size_t)BH * p.splits * Nq * d;
+  const float c = scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  const int rows = BH * Nq;
+  const unsigned merge_blocks = (unsigned)((rows + 3) / 4);
+  if (d == 128) {
+    launch_split_d<128>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
+    hipLaunchKernelGGL(dec_merge_kernel<128>, dim3(merge_blocks), dim3(256), 0, st, po, pl, (__bf16*)o, lse, rows,
+                       Nq, p.splits);
+  } else {
+    launch_split_d<64>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
+    hipLaunchKernelGGL(dec_merge_kernel<64>, dim3(merge_blocks), dim3(256), 0, st, po, pl, (__bf16*)o, lse, rows, Nq,
+                       p.splits);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace fa

@@ -25,6 +25,18 @@ int launch_fused(const void* q, const void* k, const void* v, void* o, float* ls
 int launch_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int N, int d, float scale, void* workspace, void* stream);
 
+// Key-range split of the decode-shaped forward (see fa_select.cpp).
+struct DecodePlan {
+  int splits;  // chunks per (b, h), one workgroup each
+  int chunk;   // keys per chunk (the last chunk of a head may be shorter)
+};
+DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d);
+
+// Enqueue the decode split and merge kernels; returns a fa_status code. Arguments
+// already validated; workspace holds at least fa_decode_workspace_bytes.
+int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int d, float scale, void* workspace, void* stream);
+
 // 1 if the current device is gfx950, 0 if not, negative fa_status on HIP error.
 int device_is_gfx950();
 

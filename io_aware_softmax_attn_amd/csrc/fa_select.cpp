@@ -14,6 +14,9 @@
 // registers. Four K/V stages of 2*64*d*2 bytes use 128 KB at d = 128.
 #include "fa_internal.h"
 
+#include <algorithm>
+#include <cstdint>
+
 namespace fa {
 namespace {
 
@@ -35,6 +38,29 @@ Blocks select_blocks(int d, int N, int B, int H) {
   b.br = kWaves * kRowsPerWave;
   b.bc = kKeysPerTile;
   return b;
+}
+
+// Split of the key range for the decode-shaped forward (few query rows, long K/V).
+// Each (b, h) is cut into S chunks of `chunk` keys, one workgroup per chunk, so
+// that B*H*S reaches about 2048 workgroups (8 per CU on 256 CUs: enough loads in
+// flight to cover HBM latency) without chunks shorter than 256 keys (each chunk
+// adds a partial result of Nq*(d+1) floats to write and merge). Chunks are
+// multiples of 128 keys, a whole number of the split kernel's key batches for
+// both head dimensions. Depends on the shape only, not on the device.
+DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d) {
+  (void)Nq;
+  (void)d;
+  constexpr int64_t kTargetGroups = 2048, kMinChunk = 256, kAlign = 128;
+  const int64_t bh = std::max<int64_t>(1, (int64_t)B * H);
+  const int64_t nk = std::max<int64_t>(1, Nk);
+  int64_t s = (kTargetGroups + bh - 1) / bh;
+  s = std::max<int64_t>(1, std::min(s, (nk + kMinChunk - 1) / kMinChunk));
+  int64_t chunk = (nk + s - 1) / s;
+  chunk = std::min(nk, (chunk + kAlign - 1) / kAlign * kAlign);
+  DecodePlan p;
+  p.splits = (int)((nk + chunk - 1) / chunk);
+  p.chunk = (int)chunk;
+  return p;
 }
 
 }  // namespace fa

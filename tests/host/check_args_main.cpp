@@ -36,6 +36,11 @@ int launch_unfused(const void*, const void*, const void*, void*, float*, int, in
   ++g_launches;
   return FA_OK;
 }
+int launch_decode(const void*, const void*, const void*, void*, float*, int, int, int, int, int, float, void*,
+                  void*) {
+  ++g_launches;
+  return FA_OK;
+}
 int device_is_gfx950() { return g_device; }
 }  // namespace fa
 
@@ -115,6 +120,35 @@ int main() {
   EXPECT(fa_unfused_fwd(q, k, v, o, lse, B, H, N, d, sc, ws + 8, need, nullptr) == FA_ERR_WORKSPACE);
   EXPECT(fa_unfused_fwd(q, k, v, o, lse, B, H, N, d, sc, q, need, nullptr) == FA_ERR_WORKSPACE);
   EXPECT(g_launches == before + 1);
+
+  // Decode: q/o hold Nq = 4 rows, k/v the N = 100 keys of each head.
+  {
+    g_device = 1;
+    const int nq = 4;
+    int splits = 0, chunk = 0;
+    size_t dneed = 0;
+    EXPECT(fa_decode_plan(B, H, nq, N, d, &splits, &chunk, &dneed) == FA_OK);
+    EXPECT(splits == 1 && chunk == N && dneed == ((size_t)B * H * nq * (d + 1) * 4 + 255) / 256 * 256);
+    EXPECT(fa_decode_plan(B, H, nq, N, d, nullptr, nullptr, nullptr) == FA_OK);
+    int s2 = 0, c2 = 0;
+    size_t w2 = 1;
+    EXPECT(fa_decode_plan(B, H, 17, N, d, &s2, &c2, &w2) == FA_ERR_SHAPE && w2 == 0);
+    w2 = 1;
+    EXPECT(fa_decode_plan(imax, imax, 16, 1 << 30, d, &s2, &c2, &w2) == FA_ERR_OVERFLOW && w2 == 0);
+    char* dws = static_cast<char*>(std::aligned_alloc(256, dneed));
+    const int before_dec = g_launches;
+    EXPECT(fa_decode_fwd(q, k, v, o, lse, B, H, nq, N, d, sc, dws, dneed, nullptr) == FA_OK &&
+           g_launches == before_dec + 1);
+    EXPECT(fa_decode_fwd(q, k, v, o, lse, B, H, nq, N, d, sc, dws, dneed - 1, nullptr) == FA_ERR_WORKSPACE);
+    EXPECT(fa_decode_fwd(q, k, v, o, lse, B, H, 0, N, d, sc, nullptr, 0, nullptr) == FA_OK);
+    EXPECT(fa_decode_fwd(q, k, v, o, lse, B, H, nq, 0, d, sc, dws, dneed, nullptr) == FA_ERR_SHAPE);
+    EXPECT(fa_decode_fwd(q, k, v, k, lse, B, H, nq, N, d, sc, dws, dneed, nullptr) == FA_ERR_ALIAS);
+    EXPECT(fa_decode_check_args(q, k, v, o, lse, B, H, nq, N, d, sc, v, dneed) == FA_ERR_WORKSPACE);
+    g_device = 0;
+    EXPECT(fa_decode_fwd(q, k, v, o, lse, B, H, nq, N, d, sc, dws, dneed, nullptr) == FA_ERR_DEVICE);
+    EXPECT(g_launches == before_dec + 1);
+    std::free(dws);
+  }
 
   // Selector and strings.
   int br = 0, bc = 0, nw = 0;

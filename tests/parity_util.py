@@ -82,3 +82,21 @@ def to_gpu(*ts):
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def decode_errors(q, k, v, o_gpu, lse_gpu, scale, heads=None):
+    """Errors of decode outputs against the fp64 oracle, head by head: ``heads`` is a
+    list of (b, h) pairs (None = every head); all query rows of each head are
+    compared. Returns the same keys as gpu_errors, each the maximum over the heads."""
+    B, H = q.shape[:2]
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    out = {"max_dO": 0.0, "max_dO_beyond_rounding": -1.0, "max_dLSE": 0.0, "finite": True, "E_unf": 0.0}
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        e = gpu_errors(q[sl], k[sl], v[sl], o_gpu[sl], lse_gpu[sl], scale)
+        for key in ("max_dO", "max_dO_beyond_rounding", "max_dLSE", "E_unf"):
+            out[key] = max(out[key], e[key])
+        out["finite"] = out["finite"] and e["finite"]
+    return out
+

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks", "fa_check_args",
-              "fa_status_string", "fa_version"):
+              "fa_status_string", "fa_version", "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args"):
         assert n in names
 
 
@@ -144,3 +144,78 @@ def test_python_binding_type_checks(fa):
         fa.fa_fwd(q, q, q, q.clone(), lse)
     with pytest.raises(TypeError):
         fa.fa_fwd(q.float(), q, q, q.clone(), lse)
+
+
+# ---------------------------------------------------------------------------
+# Decode-shaped forward: plan and validation (no GPU)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d", [(16, 32, 1, 8192, 128), (1, 32, 1, 131072, 128), (1, 1, 1, 1, 128),
+                                         (2, 3, 4, 1000, 64), (1, 8, 16, 30001, 128), (64, 64, 2, 100, 64),
+                                         (1, 1, 1, 1 << 30, 128)])
+def test_decode_plan_covers_every_key(fa, B, H, Nq, Nk, d):
+    splits, chunk, ws = fa.fa_decode_plan(B, H, Nq, Nk, d)
+    assert splits >= 1 and chunk >= 1
+    assert (splits - 1) * chunk < Nk <= splits * chunk  # every chunk holds at least one key
+    assert chunk == Nk or chunk % 128 == 0
+    assert ws == (B * H * splits * Nq * (d + 1) * 4 + 255) // 256 * 256
+    assert B * H * splits <= 2 ** 31 - 1
+
+
+def test_decode_plan_fills_the_chip(fa):
+    # Enough workgroups for 256 CUs when the keys allow it; no chunk below 256 keys
+    # unless the whole sequence is shorter.
+    for B, H, Nk in ((16, 32, 8192), (1, 32, 131072), (1, 1, 1 << 20), (4, 16, 4096)):
+        splits, chunk, _ = fa.fa_decode_plan(B, H, 1, Nk, 128)
+        assert B * H * splits >= 2048 or chunk <= 384
+        assert chunk >= 256 or chunk == Nk
+
+
+def test_decode_plan_errors(fa):
+    with pytest.raises(ValueError):
+        fa.fa_decode_plan(1, 1, 17, 100, 128)
+    with pytest.raises(ValueError):
+        fa.fa_decode_plan(1, 1, 1, 100, 96)
+    with pytest.raises(ValueError):
+        fa.fa_decode_plan(1, 1, 1, (1 << 30) + 1, 128)
+
+
+def dcheck(fa, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=2, Nq=4, Nk=300, d=128, scale=0.1,
+           wsp=16 * A, wsb=None):
+    if wsb is None:
+        wsb = fa.fa_decode_plan(B, H, Nq, Nk, d)[2] if 0 <= Nq <= 16 and Nk >= 0 and d in (64, 128) else 0
+    return fa.fa_decode_check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, wsp, wsb)
+
+
+def test_decode_check_args(fa):
+    S = fa.STATUS
+    assert dcheck(fa) == 0
+    assert dcheck(fa, q=A, k=A, v=A) == 0
+    assert dcheck(fa, Nq=0, q=None, k=None, v=None, o=None, lse=None, wsp=None) == 0  # empty
+    assert dcheck(fa, B=0, wsp=None) == 0
+    assert dcheck(fa, Nq=17) == S["FA_ERR_SHAPE"]
+    assert dcheck(fa, Nk=0) == S["FA_ERR_SHAPE"]
+    assert dcheck(fa, Nk=(1 << 30) + 1, wsb=1 << 40) == S["FA_ERR_SHAPE"]
+    assert dcheck(fa, Nq=-1, wsb=0) == S["FA_ERR_SHAPE"]
+    assert dcheck(fa, d=96) == S["FA_ERR_HEADDIM"]
+    assert dcheck(fa, scale=float("nan")) == S["FA_ERR_SCALE"]
+    assert dcheck(fa, v=None) == S["FA_ERR_NULL"]
+    assert dcheck(fa, k=2 * A + 8) == S["FA_ERR_ALIGN"]
+    assert dcheck(fa, lse=5 * A + 1) == S["FA_ERR_ALIGN"]
+    assert dcheck(fa, o=2 * A + 4096) == S["FA_ERR_ALIAS"]  # inside k (2*300*128*2 bytes)
+    assert dcheck(fa, lse=4 * A + 16) == S["FA_ERR_ALIAS"]  # inside o
+    assert dcheck(fa, wsp=None) == S["FA_ERR_WORKSPACE"]
+    need = fa.fa_decode_plan(1, 2, 4, 300, 128)[2]
+    assert dcheck(fa, wsb=need - 1) == S["FA_ERR_WORKSPACE"]
+    assert dcheck(fa, wsp=16 * A + 8) == S["FA_ERR_WORKSPACE"]
+    assert dcheck(fa, wsp=3 * A) == S["FA_ERR_WORKSPACE"]  # overlaps v
+    assert dcheck(fa, B=1 << 30, H=1 << 30, wsb=0) == S["FA_ERR_OVERFLOW"]
+
+
+def test_decode_fwd_rejects_before_any_hip_call(fa):
+    S = fa.STATUS
+    lib = fa.lib
+    assert lib.fa_decode_fwd(A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 1, 32, 100, 128, 0.1, 16 * A, 1 << 20,
+                             None) == S["FA_ERR_SHAPE"]
+    assert lib.fa_decode_fwd(None, None, None, None, None, 1, 1, 0, 100, 128, 0.1, None, 0, None) == 0
+
