@@ -41,19 +41,27 @@ Blocks select_blocks(int d, int N, int B, int H) {
 }
 
 // Split of the key range for the decode-shaped forward (few query rows, long K/V).
-// Each (b, h) is cut into S chunks of `chunk` keys, one workgroup per chunk, so
-// that B*H*S reaches about 2048 workgroups (8 per CU on 256 CUs: enough loads in
-// flight to cover HBM latency) without chunks shorter than 256 keys (each chunk
-// adds a partial result of Nq*(d+1) floats to write and merge). Chunks are
-// multiples of 128 keys, a whole number of the split kernel's key batches for
-// both head dimensions. Depends on the shape only, not on the device.
+// Each (b, h) is cut into S chunks of `chunk` keys, one workgroup per chunk. The
+// split kernel streams K and V, so the grid aims at one full round of resident
+// workgroups: 256 CUs times the workgroups one CU holds at once, which the kernel's
+// register use sets per compiled row count (70, 80, 110, 170 and 256 VGPRs for up
+// to 1, 2, 4, 8 and 16 query rows: 7, 6, 4, 2 and 1 workgroups of 4 waves). A
+// second, partial round would leave most CUs idle at the end; more, shorter chunks
+// add partial results to write and merge. Chunks hold at least 256 keys and are
+// multiples of 128 keys, a whole number of the kernel's key batches for both head
+// dimensions. Depends on the shape only, not on the device.
+namespace {
+constexpr int kCus = 256;
+int resident_per_cu(int Nq) { return Nq <= 1 ? 7 : Nq <= 2 ? 6 : Nq <= 4 ? 4 : Nq <= 8 ? 2 : 1; }
+}  // namespace
+
 DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d) {
-  (void)Nq;
   (void)d;
-  constexpr int64_t kTargetGroups = 2048, kMinChunk = 256, kAlign = 128;
+  constexpr int64_t kMinChunk = 256, kAlign = 128;
+  const int64_t target = (int64_t)kCus * resident_per_cu(Nq);
   const int64_t bh = std::max<int64_t>(1, (int64_t)B * H);
   const int64_t nk = std::max<int64_t>(1, Nk);
-  int64_t s = (kTargetGroups + bh - 1) / bh;
+  int64_t s = (target + bh - 1) / bh;
   s = std::max<int64_t>(1, std::min(s, (nk + kMinChunk - 1) / kMinChunk));
   int64_t chunk = (nk + s - 1) / s;
   chunk = std::min(nk, (chunk + kAlign - 1) / kAlign * kAlign);

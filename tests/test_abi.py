@@ -163,12 +163,20 @@ def test_decode_plan_covers_every_key(fa, B, H, Nq, Nk, d):
 
 
 def test_decode_plan_fills_the_chip(fa):
-    # Enough workgroups for 256 CUs when the keys allow it; no chunk below 256 keys
+    # About one round of resident workgroups (256 CUs x 7, 6, 4, 2, 1 per CU for up
+    # to 1, 2, 4, 8, 16 query rows) when the keys allow it; no chunk below 256 keys
     # unless the whole sequence is shorter.
-    for B, H, Nk in ((16, 32, 8192), (1, 32, 131072), (1, 1, 1 << 20), (4, 16, 4096)):
-        splits, chunk, _ = fa.fa_decode_plan(B, H, 1, Nk, 128)
-        assert B * H * splits >= 2048 or chunk <= 384
-        assert chunk >= 256 or chunk == Nk
+    resident = {1: 7, 2: 6, 3: 4, 4: 4, 8: 2, 16: 1}
+    for B, H, Nk in ((16, 32, 8192), (1, 32, 131072), (1, 1, 1 << 20), (4, 16, 4096), (2, 8, 30001)):
+        for nq, per_cu in resident.items():
+            splits, chunk, _ = fa.fa_decode_plan(B, H, nq, Nk, 128)
+            target = 256 * per_cu
+            # splits per head: what the target asks for, at most one chunk of 256 keys
+            # each, then chunks rounded up to 128 keys
+            want = min(-(-target // (B * H)), -(-Nk // 256))
+            chunk_want = min(Nk, -(-(-(-Nk // want)) // 128) * 128)
+            assert chunk == chunk_want and splits == -(-Nk // chunk_want), (B, H, Nk, nq)
+            assert chunk >= 256 or chunk == Nk
 
 
 def test_decode_plan_errors(fa):
