@@ -1,6 +1,8 @@
 """Compile the HIP sources of this package into ``libfa.so`` (gfx950 only).
 
-Run ``python -m io_aware_softmax_attn_amd.build`` or call :func:`build_library`.
+Run ``python io_aware_softmax_attn_amd/build.py`` or call :func:`build_library`
+from a module loaded on its own (importing the package first would load the
+library that is about to be replaced).
 The library is written next to this file, in-tree, through a temporary name and
 an atomic rename, so a half-written file is never loaded.
 """
