@@ -168,6 +168,62 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, dec
     print(json.dumps(rec))
 
 
+IO_SWEEP_ORDERS = (0, 1, 2)
+IO_SWEEP_LENGTHS = (2048, 4096, 8192, 16384)
+IO_SWEEP_SHAPE = (1, 32, 128)  # B, H, d
+IO_SWEEP_CMD = ("rocprofv3 --pmc {ctr} -d {dir}/pmc_o{order}_n{n}_{ctr} -o c --output-format csv -- "
+                "python3 bench.py --shape {B},{H},{n},{d} --tile-order {order} --steps 2 --warmup 1 "
+                "--launches-only --copy-calibration 1073741824")
+
+
+def summarize_io_sweep(sweep_dir, copy_bytes):
+    """HBM traffic of the fused kernel per workgroup-to-tile order and sequence
+    length, from FETCH_SIZE / WRITE_SIZE runs made with IO_SWEEP_CMD, written to
+    profiles/fa_fwd_io_sweep.md next to two models: every byte once, and every
+    query tile re-reading its head's K and V."""
+    B, H, d = IO_SWEEP_SHAPE
+    names = {0: "XCD-aware (fa_fwd)", 1: "dispatch order", 2: "query-tile-major"}
+    rows = []
+    for order in IO_SWEEP_ORDERS:
+        for n in IO_SWEEP_LENGTHS:
+            vals = {}
+            for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                table = _read_counter_csv(os.path.join(sweep_dir, f"pmc_o{order}_n{n}_{ctr}", "c_counter_collection.csv"))
+                fa_vals = [v for (kname, c), vs in table.items() if c == ctr and "fa_fwd_kernel" in kname for v in vs]
+                copy = [v for (kname, c), vs in table.items() if c == ctr and "fa_fwd_kernel" not in kname for v in vs]
+                vals[ctr] = sum(fa_vals) / len(fa_vals) * copy_bytes / copy[0]
+            total = vals["FETCH_SIZE"] + vals["WRITE_SIZE"]
+            minimum = B * H * n * (8 * d + 4)
+            tiles = -(-n // 256)
+            reread = B * H * (tiles * 4 * n * d + n * (4 * d + 4))  # K, V per query tile; Q, O, LSE once
+            rows.append((order, n, total, minimum, reread))
+    lines = [
+        "# Fused-kernel HBM traffic by workgroup-to-tile order and sequence length",
+        "",
+        f"B={B} H={H} d={d}, 256 query rows per workgroup. Bytes per launch from FETCH_SIZE + WRITE_SIZE "
+        "(KiB per dispatch), each scaled by what the counter reads for a 1 GiB device-to-device copy in the "
+        "same run, averaged over the 3 launches of each run. One run per order, length and counter:",
+        "",
+        "```",
+        IO_SWEEP_CMD.format(ctr="<FETCH_SIZE|WRITE_SIZE>", dir="gpurun_out/io_sweep", order="<order>", n="<N>",
+                            B=B, H=H, d=d),
+        "```",
+        "",
+        "Models: `once` = B*H*N*(8d+4) (Q, K, V read once, O and LSE written once); `re-read` = K and V "
+        "read again by every query tile of their head, ceil(N/256) times, plus Q, O, LSE once.",
+        "",
+        "| order | N | bytes per launch | / once | / re-read |",
+        "|---|---|---|---|---|",
+    ]
+    for order, n, total, minimum, reread in rows:
+        lines.append(f"| {order} {names[order]} | {n} | {total:,.0f} | {total / minimum:.3f} | {total / reread:.3f} |")
+    lines += ["", f"Kernel source sha256[:16] of fa_fwd.hip: {kernel_source_hash()}."]
+    path = os.path.join(ROOT, "profiles", "fa_fwd_io_sweep.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(stats_csv, command, workload):
     """Write the per-kernel duration summary of a rocprofv3 --stats run, with the
     command that produced it and the algorithmic rate at the average duration."""
@@ -411,6 +467,13 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="no GPU work: turn a rocprofv3 --kernel-trace --stats kernel_stats.csv into "
                          "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin")
+    ap.add_argument("--tile-order", type=int, default=0, choices=(0, 1, 2),
+                    help="fused path only: workgroup-to-tile order of fa_fwd_tile_order (0 = fa_fwd's)")
+    ap.add_argument("--shape", metavar="B,H,N,d",
+                    help="a fused-path shape outside the named workloads (seed 0, unit Gaussian inputs)")
+    ap.add_argument("--summarize-io-sweep", metavar="DIR",
+                    help="no GPU work: turn the FETCH_SIZE/WRITE_SIZE runs of the tile-order sweep under DIR "
+                         "into profiles/fa_fwd_io_sweep.md (with --copy-calibration BYTES)")
     ap.add_argument("--decode", action="store_true",
                     help="the decode-shaped forward (few queries against many keys) instead of the prefill "
                          "benchmark; also selects the decode kernels for --summarize-pmc")
@@ -422,6 +485,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_calibration,
                       unfused=args.unfused, decode=args.decode)
+        return
+    if args.summarize_io_sweep:
+        summarize_io_sweep(args.summarize_io_sweep, args.copy_calibration)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload)
@@ -449,7 +515,11 @@ def main():
     import attn_inputs
     import io_aware_softmax_attn_amd as fa
 
-    w = attn_inputs.HEADLINE if args.workload is None else attn_inputs.WORKLOAD_BY_NAME[args.workload]
+    if args.shape:
+        B, H, N, d = (int(x) for x in args.shape.split(","))
+        w = attn_inputs.Workload(f"b{B}h{H}_n{N}_d{d}", B, H, N, d, seed=0)
+    else:
+        w = attn_inputs.HEADLINE if args.workload is None else attn_inputs.WORKLOAD_BY_NAME[args.workload]
     q, k, v = attn_inputs.make_workload(w)
     dev = torch.device("cuda:0")
     qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
@@ -470,6 +540,8 @@ def main():
     def launch():
         if args.unfused:
             fa.fa_unfused_fwd(qg, kg, vg, o, lse, ws, scale=w.scale, stream=stream)
+        elif args.tile_order:
+            fa.fa_fwd_tile_order(qg, kg, vg, o, lse, args.tile_order, scale=w.scale, stream=stream)
         else:
             fa.fa_fwd(qg, kg, vg, o, lse, scale=w.scale, stream=stream)
 
@@ -506,7 +578,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False,
-                   "path": "unfused-3-kernel" if args.unfused else "fused"},
+                   "path": "unfused-3-kernel" if args.unfused else "fused",
+                   **({"tile_order": args.tile_order} if args.tile_order else {})},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),

@@ -71,6 +71,24 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, void* stream);
 
 /*
+ * fa_fwd with an explicit order in which workgroups take the (b, h, query tile)
+ * tiles, for measuring how the reuse of K/V across a head's query tiles in the
+ * on-chip caches sets the memory traffic. The pages count the traffic of the
+ * tiled method as K and V re-read once per query tile, about N^2 d^2 / M element
+ * accesses for on-chip memory M ("01 · 注意力为什么是 IO 瓶颈", section 7), and
+ * O(N d) when those re-reads are served on chip (same page, section 4).
+ *   order 0: fa_fwd's order: each XCD takes a contiguous range of tiles, so a
+ *            head's query tiles share that XCD's L2;
+ *   order 1: dispatch order: a head's consecutive tiles go to all 8 XCDs;
+ *   order 2: query-tile-major: consecutive workgroups belong to different heads,
+ *            so a head's tiles are spread over XCDs and time.
+ * Results are bitwise identical for every order. Returns FA_ERR_SHAPE for an
+ * order outside 0..2; otherwise as fa_fwd.
+ */
+int fa_fwd_tile_order(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int N, int d, float scale, int order, void* stream);
+
+/*
  * The textbook three-step forward ("01 · 注意力为什么是 IO 瓶颈", section 3
  * table and section 5): kernel 1 writes S = scale*QK^T (fp32, [B,H,N,Ns]) to the
  * workspace, kernel 2 reads S and writes P = softmax(S) (bf16, [B,H,N,Ns]) and

@@ -21,10 +21,12 @@ __all__ = [
     "FaError", "lib", "fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks",
     "fa_check_args", "fa_status_string", "fa_version", "forward", "unfused_forward",
     "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args", "decode_forward", "DECODE_MAX_NQ",
+    "fa_fwd_tile_order", "TILE_ORDERS",
     "STATUS",
 ]
 
 DECODE_MAX_NQ = 16  # FA_DECODE_MAX_NQ
+TILE_ORDERS = {"xcd": 0, "dispatch": 1, "qtile_major": 2}  # orders of fa_fwd_tile_order
 
 STATUS = {
     "FA_OK": 0, "FA_ERR_NULL": -1, "FA_ERR_SHAPE": -2, "FA_ERR_HEADDIM": -3, "FA_ERR_ALIGN": -4,
@@ -61,6 +63,8 @@ def _load() -> ctypes.CDLL:
     dll.fa_select_blocks.restype = i
     dll.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz]
     dll.fa_check_args.restype = i
+    dll.fa_fwd_tile_order.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    dll.fa_fwd_tile_order.restype = i
     dll.fa_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp]
     dll.fa_decode_fwd.restype = i
     dll.fa_decode_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(sz)]
@@ -159,6 +163,19 @@ def fa_fwd(q, k, v, o, lse, scale=None, stream=None):
     with torch.cuda.device(q.device):  # the library launches on the current device
         _raise(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                           _stream_handle(stream, q.device)), "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_tile_order(q, k, v, o, lse, order, scale=None, stream=None):
+    """fa_fwd with an explicit workgroup-to-tile order (0, 1, 2 or a TILE_ORDERS
+    name), for traffic measurements; results are identical for every order."""
+    B, H, N, d = _shape_of(q, k, v, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    order = TILE_ORDERS.get(order, order)
+    with torch.cuda.device(q.device):
+        _raise(lib.fa_fwd_tile_order(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                     int(order), _stream_handle(stream, q.device)), "fa_fwd_tile_order")
     return o, lse
 
 

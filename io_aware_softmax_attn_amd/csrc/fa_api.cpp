@@ -184,6 +184,18 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return fa::launch_fused(q, k, v, o, lse, B, H, N, d, scale, fa::select_blocks(d, N, B, H), stream);
 }
 
+int fa_fwd_tile_order(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                      float scale, int order, void* stream) {
+  if (order < 0 || order > 2) return FA_ERR_SHAPE;
+  const int st = fa_check_args(q, k, v, o, lse, B, H, N, d, scale, 0, nullptr, 0);
+  if (st != FA_OK) return st;
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)N == 0) return FA_OK;
+  const int dev = fa::device_is_gfx950();
+  if (dev < 0) return dev;
+  if (dev == 0) return FA_ERR_DEVICE;
+  return fa::launch_fused(q, k, v, o, lse, B, H, N, d, scale, fa::select_blocks(d, N, B, H), stream, order);
+}
+
 int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                    float scale, void* workspace, size_t workspace_bytes, void* stream) {
   const int st = fa_check_args(q, k, v, o, lse, B, H, N, d, scale, 1, workspace, workspace_bytes);

@@ -115,6 +115,20 @@ __device__ __forceinline__ int remap_xcd(int w, int total) {
   return xcd < rem ? xcd * (base + 1) + idx : rem * (base + 1) + (xcd - rem) * base + idx;
 }
 
+// Logical tile id (bh * tiles_per_head + query tile) of workgroup w under a tile
+// order (the orders of fa_fwd_tile_order): 0 keeps each head's tiles on one XCD;
+// 1 takes them in dispatch order, so the dispatcher deals a head's consecutive
+// tiles to all 8 XCDs; 2 runs query-tile-major (consecutive workgroups belong to
+// different heads), so the tiles of one head are spread over time and XCDs.
+__device__ __forceinline__ int tile_of(int w, int total, int tiles_per_head, int order) {
+  if (order == 1) return w;
+  if (order == 2) {
+    const int bhs = total / tiles_per_head;
+    return (w % bhs) * tiles_per_head + w / bhs;
+  }
+  return remap_xcd(w, total);
+}
+
 // v_permlane32_swap with both operands = x: lanes 0-31 receive lanes 32-63 in one
 // result and vice versa, so max/sum of the two results reduces over lanes l, l^32.
 __device__ __forceinline__ float pair_max(float x) {
@@ -663,7 +677,7 @@ template <int D>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
               __bf16* __restrict__ o, float* __restrict__ lse, int N, int tiles_per_head, int total_tiles,
-              float c /* scale * log2(e) */) {
+              float c /* scale * log2(e) */, int order) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
   // The LDS base as a scalar: every LDS address below is a scalar offset plus at
@@ -673,7 +687,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5;  // which half of the wave
-  const int logical = remap_xcd(blockIdx.x, total_tiles);
+  const int logical = tile_of(blockIdx.x, total_tiles, tiles_per_head, order);
   const int bh = logical / tiles_per_head;
   const int qtile = logical - bh * tiles_per_head;
   const size_t head_off = (size_t)bh * (size_t)N * D;
@@ -920,7 +934,7 @@ int device_is_gfx950() {
 }
 
 int launch_fused(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                 float scale, const Blocks& blk, void* stream) {
+                 float scale, const Blocks& blk, void* stream, int order) {
   (void)blk;
   const int tiles = (N + 255) / 256;
   const long long total = (long long)B * H * tiles;
@@ -928,10 +942,10 @@ int launch_fused(const void* q, const void* k, const void* v, void* o, float* ls
   hipStream_t s = (hipStream_t)stream;
   if (d == 128) {
     hipLaunchKernelGGL(fa_fwd_kernel<128>, dim3((unsigned)total), dim3(256), 0, s, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, tiles, (int)total, c);
+                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, tiles, (int)total, c, order);
   } else {
     hipLaunchKernelGGL(fa_fwd_kernel<64>, dim3((unsigned)total), dim3(256), 0, s, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, tiles, (int)total, c);
+                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, tiles, (int)total, c, order);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

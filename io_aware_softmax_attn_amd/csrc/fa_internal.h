@@ -18,8 +18,9 @@ struct Blocks {
 Blocks select_blocks(int d, int N, int B, int H);
 
 // Enqueue the fused forward; returns a fa_status code. Arguments already validated.
+// order: workgroup-to-tile order (0 = XCD-aware, the default; see fa_fwd_tile_order).
 int launch_fused(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int B, int H, int N, int d, float scale, const Blocks& blk, void* stream);
+                 int B, int H, int N, int d, float scale, const Blocks& blk, void* stream, int order = 0);
 
 // Enqueue the three unfused kernels; returns a fa_status code.
 int launch_unfused(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks", "fa_check_args",
-              "fa_status_string", "fa_version", "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args"):
+              "fa_status_string", "fa_version", "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args",
+              "fa_fwd_tile_order"):
         assert n in names
 
 
@@ -226,4 +227,14 @@ def test_decode_fwd_rejects_before_any_hip_call(fa):
     assert lib.fa_decode_fwd(A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 1, 32, 100, 128, 0.1, 16 * A, 1 << 20,
                              None) == S["FA_ERR_SHAPE"]
     assert lib.fa_decode_fwd(None, None, None, None, None, 1, 1, 0, 100, 128, 0.1, None, 0, None) == 0
+
+
+def test_tile_order_rejects_before_any_hip_call(fa):
+    S = fa.STATUS
+    lib = fa.lib
+    for order in (-1, 3):
+        assert lib.fa_fwd_tile_order(A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 1, 64, 128, 0.1, order, None) == \
+            S["FA_ERR_SHAPE"]
+    assert lib.fa_fwd_tile_order(A, 2 * A, 3 * A, A, 5 * A, 1, 1, 64, 128, 0.1, 1, None) == S["FA_ERR_ALIAS"]
+    assert lib.fa_fwd_tile_order(None, None, None, None, None, 1, 1, 0, 128, 0.1, 2, None) == 0
 

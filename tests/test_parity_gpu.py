@@ -225,3 +225,18 @@ def test_v_power_of_two_scaling_is_exact(fa, d):
     o2, l2 = run_fused(fa, q, k, vs, default_scale(d))
     assert torch.equal(l1, l2)
     assert torch.equal(o2.float(), (o1.float() * 2.0 ** 100).to(torch.bfloat16).float())
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 3, 1000, 128), (2, 5, 777, 64), (1, 32, 2048, 128)])
+def test_tile_orders_give_identical_results(fa, B, H, N, d):
+    """Each (b, h, query tile) is computed the same way wherever and whenever it runs,
+    so every workgroup-to-tile order gives bitwise the same O and LSE."""
+    announce(f"tile orders B={B} H={H} N={N} d={d}")
+    q, k, v = to_gpu(*attn_inputs.make_qkv(B, H, N, d, seed=N + d))
+    ref_o, ref_l = fa.forward(q, k, v)
+    for order in (1, 2):
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        fa.fa_fwd_tile_order(q, k, v, o, lse, order)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l), order
