@@ -15,10 +15,14 @@ Sources (the three pages on IO-aware softmax attention):
   * The same update (steps 2 and 4-5) applied to whole key chunks: the merge of
     partial results of the split over keys (attention_split_fp64).
 
+backward.py holds the gradients of the forward (the chain rule through its three
+steps; the pages give no backward formulas, see its docstring).
+
 Every function is pinned by tests that do not re-type its formulas (closed forms,
 invariants, brute force, library special cases); no function here is "parity
 unpinned".
 """
+from .backward import attention_backward_fp64, attention_backward_unfused_bf16  # noqa: F401
 from .attention import (  # noqa: F401
     attention_fp64,
     attention_online_fp64,
