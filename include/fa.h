@@ -162,6 +162,30 @@ int fa_decode_check_args(const void* q, const void* k, const void* v, const void
                          int B, int H, int Nq, int Nk, int d, float scale,
                          const void* workspace, size_t workspace_bytes);
 
+/*
+ * Attention backward: dq, dk, dv (bf16 [B,H,N,d]) of o = fa_fwd(q, k, v) for the
+ * upstream gradient dO (bf16 [B,H,N,d]), from q, k, v and the forward's o and lse:
+ *   dv = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dq = scale dS K,  dk = scale dS^T Q
+ * with P = exp(scale Q K^T - lse) recomputed tile by tile and D_i = dO_i . o_i. The
+ * pages keep only O and the per-row LSE from the forward and recompute P in the
+ * backward ("01 · 注意力为什么是 IO 瓶颈", section 6); no N x N matrix is stored.
+ * lse receives no gradient. Same conventions as fa_fwd for shapes, d, scale and
+ * alignment; dq, dk and dv must not overlap each other or any input; workspace is
+ * a caller-owned device buffer of at least fa_bwd_workspace_bytes(B, H, N) bytes,
+ * 16-byte aligned, overlapping no tensor argument. Three kernels: per-row D and
+ * lse in log2 units into the workspace; dq (one workgroup per 128 query rows); dk
+ * and dv (one workgroup per 128 keys). Products are bf16 MFMA with fp32
+ * accumulation; P and dS enter them rounded to bf16; outputs are rounded to bf16
+ * once. Deterministic: no atomics.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_bwd needs: 8*B*H*N (fp32 D and lse in log2 units per row),
+ * rounded up to 256; 0 if negative or the product overflows size_t. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);
 

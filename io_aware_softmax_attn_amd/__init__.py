@@ -21,7 +21,7 @@ __all__ = [
     "FaError", "lib", "fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks",
     "fa_check_args", "fa_status_string", "fa_version", "forward", "unfused_forward",
     "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args", "decode_forward", "DECODE_MAX_NQ",
-    "fa_fwd_tile_order", "TILE_ORDERS",
+    "fa_fwd_tile_order", "TILE_ORDERS", "fa_bwd", "fa_bwd_workspace_bytes", "backward",
     "STATUS",
 ]
 
@@ -63,6 +63,10 @@ def _load() -> ctypes.CDLL:
     dll.fa_select_blocks.restype = i
     dll.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz]
     dll.fa_check_args.restype = i
+    dll.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
+    dll.fa_bwd.restype = i
+    dll.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+    dll.fa_bwd_workspace_bytes.restype = sz
     dll.fa_fwd_tile_order.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     dll.fa_fwd_tile_order.restype = i
     dll.fa_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp]
@@ -265,3 +269,39 @@ def decode_forward(q, k, v, scale=None, stream=None):
     _, _, ws_bytes = fa_decode_plan(B, H, Nq, k.shape[2], d)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
     return fa_decode_fwd(q, k, v, o, lse, ws, scale=scale, stream=stream)
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return lib.fa_bwd_workspace_bytes(int(B), int(H), int(N))
+
+
+def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, scale=None, stream=None):
+    """Backward into caller-provided dq, dk, dv (bf16, shaped like q) from the
+    forward's o and lse and the upstream dO; workspace: uint8 GPU tensor of at least
+    fa_bwd_workspace_bytes(B, H, N) bytes."""
+    B, H, N, d = _shape_of(q, k, v, o, lse)
+    _check_tensors(dO, dq, dk, dv, lse)
+    for name, t in (("dO", dO), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{name} must have q's shape and device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    if workspace.device != q.device:
+        raise ValueError("workspace must be on the same GPU as the tensors")
+    nbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _raise(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+                          B, H, N, d, float(scale), _ptr(workspace), nbytes, _stream_handle(stream, q.device)),
+               "fa_bwd")
+    return dq, dk, dv
+
+
+def backward(q, k, v, o, lse, dO, scale=None, stream=None):
+    """Allocate dq, dk, dv and the workspace and run :func:`fa_bwd`. Returns (dq, dk, dv)."""
+    B, H, N, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(fa_bwd_workspace_bytes(B, H, N), 256), dtype=torch.uint8, device=q.device)
+    return fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws, scale=scale, stream=stream)
+

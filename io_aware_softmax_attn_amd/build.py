@@ -17,7 +17,7 @@ import tempfile
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_unfused.hip", "fa_decode.hip", "fa_api.cpp", "fa_select.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_unfused.hip", "fa_decode.hip", "fa_bwd.hip", "fa_api.cpp", "fa_select.cpp"]
 ARCH = "gfx950"
 
 

@@ -184,6 +184,54 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return fa::launch_fused(q, k, v, o, lse, B, H, N, d, scale, fa::select_blocks(d, N, B, H), stream);
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 0 || H < 0 || N < 0) return 0;
+  uint64_t rows, bytes;
+  if (!mul_ok((uint64_t)B * (uint64_t)H, (uint64_t)N, &rows) || !mul_ok(rows, 8, &bytes) ||
+      bytes > std::numeric_limits<uint64_t>::max() - 255)
+    return 0;
+  bytes = (bytes + 255) & ~uint64_t(255);
+  if (bytes > std::numeric_limits<size_t>::max()) return 0;
+  return (size_t)bytes;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+           void* dk, void* dv, int B, int H, int N, int d, float scale, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  // q, k, v, o, lse as the forward's arguments (o and lse are inputs here).
+  const int st = fa_check_args(q, k, v, o, lse, B, H, N, d, scale, 0, nullptr, 0);
+  if (st != FA_OK) return st;
+  const uint64_t rows64 = (uint64_t)B * (uint64_t)H * (uint64_t)N;
+  if (rows64 == 0) return FA_OK;
+  if (!dO || !dq || !dk || !dv) return FA_ERR_NULL;
+  // Launch grid: one workgroup per (b, h, 128 rows).
+  if ((uint64_t)B * (uint64_t)H * (((uint64_t)N + 127) / 128) > (uint64_t)std::numeric_limits<int32_t>::max())
+    return FA_ERR_OVERFLOW;
+  auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
+  if (misaligned(dO, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16)) return FA_ERR_ALIGN;
+  const size_t tb = (size_t)(rows64 * (uint64_t)d * 2), lb = (size_t)(rows64 * 4);
+  const void* ins[6] = {q, k, v, o, lse, dO};
+  const size_t in_bytes[6] = {tb, tb, tb, tb, lb, tb};
+  void* outs[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], tb, ins[j], in_bytes[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], tb, outs[j], tb)) return FA_ERR_ALIAS;
+  }
+  const size_t need = fa_bwd_workspace_bytes(B, H, N);
+  if (need == 0) return FA_ERR_OVERFLOW;
+  if (!workspace || workspace_bytes < need || misaligned(workspace, 16)) return FA_ERR_WORKSPACE;
+  for (int j = 0; j < 6; ++j)
+    if (overlaps(workspace, need, ins[j], in_bytes[j])) return FA_ERR_WORKSPACE;
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(workspace, need, outs[i], tb)) return FA_ERR_WORKSPACE;
+  const int dev = fa::device_is_gfx950();
+  if (dev < 0) return dev;
+  if (dev == 0) return FA_ERR_DEVICE;
+  return fa::launch_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, workspace, stream);
+}
+
 int fa_fwd_tile_order(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                       float scale, int order, void* stream) {
   if (order < 0 || order > 2) return FA_ERR_SHAPE;

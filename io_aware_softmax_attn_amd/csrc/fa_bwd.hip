@@ -1,0 +1,416 @@
+// Attention backward on gfx950: dQ, dK, dV of O = softmax(scale * Q K^T) V for an
+// upstream dO, from Q, K, V and the forward's O and LSE.
+//
+// The pages keep only O and the per-row LSE from the forward and recompute P in
+// the backward instead of storing it ("01 · 注意力为什么是 IO 瓶颈", section 6), so
+// no N x N matrix is stored here either. Per (b, h), with P = exp(S - LSE):
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q
+// where D_i = dO_i . O_i equals sum_j P_ij dP_ij (the softmax Jacobian's row term).
+//
+// Three kernels:
+//   bwd_pre   D (fp32) and LSE in log2 units, per query row, into the workspace;
+//   bwd_dq    one workgroup per 128 query rows: streams 32-key K/V tiles through
+//             LDS, recomputes S^T = K Q^T and dP^T = V dO^T, and accumulates
+//             dQ^T += K^T dS^T (the forward kernel's orientation: each lane owns one
+//             query column, K^T comes from LDS through transposing reads);
+//   bwd_dkdv  one workgroup per 128 keys, K and V held in registers: streams
+//             32-row Q/dO tiles through LDS, recomputes S = Q K^T and dP = dO V^T, and
+//             accumulates dV^T += dO^T P and dK^T += Q^T dS (each lane owns one key
+//             column; dO^T and Q^T come from LDS through transposing reads).
+// All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS enter
+// them as bf16 (nearest-even). The row order inside a 32-row block of the operand
+// read from LDS as rows is permuted (bits 2 and 3 swapped), which makes the
+// accumulator layout of S (or S^T) equal to the operand layout of the next
+// product's transposing read, as in the forward kernel.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// LDS tile layout: rows of D bf16 as D/8 16-byte chunks, the chunk index XORed
+// with a function of the row's low 4 bits, so that 16-row reads of one chunk and
+// the 4-row transposing reads both spread over the LDS banks (the same layout as
+// the forward kernel's K/V stages; 16-row-aligned offsets keep it).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+}
+template <int D>
+__device__ __forceinline__ int chunk_offset(int row, int chunk) {
+  return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
+}
+// Operand row rho of a 32-row block reads tile row pi(rho): bits 2 and 3 swapped.
+__device__ __forceinline__ int pi_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Tile row held by accumulator register i of a lane in half g (g = lane / 32) after
+// a product whose rows were read through pi_row: pi(8*(i/4) + 4g + i%4).
+__device__ __forceinline__ constexpr int acc_row(int i, int g) {
+  return 16 * (i >> 3) + 8 * g + 4 * ((i >> 2) & 1) + (i & 3);
+}
+
+__device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight accumulator values -> one bf16x8 operand (nearest-even), element order kept.
+__device__ __forceinline__ bf16x8_t pack8(const float* x) {
+  const bf16x2_t p0 = __builtin_convertvector((f32x2_t){x[0], x[1]}, bf16x2_t);
+  const bf16x2_t p1 = __builtin_convertvector((f32x2_t){x[2], x[3]}, bf16x2_t);
+  const bf16x2_t p2 = __builtin_convertvector((f32x2_t){x[4], x[5]}, bf16x2_t);
+  const bf16x2_t p3 = __builtin_convertvector((f32x2_t){x[6], x[7]}, bf16x2_t);
+  return __builtin_bit_cast(bf16x8_t, (u32x4_t){__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1),
+                                                  __builtin_bit_cast(unsigned, p2), __builtin_bit_cast(unsigned, p3)});
+}
+
+// Transposing read of a 32 x 32 block of a row-major LDS tile: lane l receives the
+// 8 values of column c0 + l%32 in rows r0 + 8g .. r0 + 8g + 7 (g = l/32), the A
+// operand of a product that contracts over those rows. r0 is a multiple of 16.
+template <int D>
+__device__ __forceinline__ bf16x8_t read_tr(unsigned tile, int r0, int c0, int lane) {
+  const int g = lane >> 5;
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int row = r0 + 8 * g + ((lane & 15) >> 2);
+  const unsigned a0 = tile + chunk_offset<D>(row, col >> 3) + 2 * (col & 7);
+  const unsigned a1 = tile + chunk_offset<D>(row + 4, col >> 3) + 2 * (col & 7);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)a0);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)a1);
+  return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5,
+                                 6, 7);
+}
+
+// Row-operand read: lane l receives chunk (2*ks + g) of tile row pi(l % 32).
+template <int D>
+__device__ __forceinline__ bf16x8_t read_row(unsigned tile, int ks, int lane) {
+  return *(const LDS_AS bf16x8_t*)(uintptr_t)(tile + chunk_offset<D>(pi_row(lane & 31), 2 * ks + (lane >> 5)));
+}
+
+// Cooperative copy of `rows` consecutive rows (from row0 of a [N, D] head; rows past
+// N read as zero) into an LDS tile, one 16-byte chunk per thread per step. The
+// values are returned in registers first (load) and written later (store), so the
+// global loads of the next tile overlap the current tile's products.
+template <int D, int kRows>
+struct TileCopy {
+  static constexpr int kChunks = D / 8;
+  static constexpr int kPerThread = kRows * kChunks / 256;
+  static_assert(kRows * kChunks % 256 == 0, "tile must split evenly over 256 threads");
+  u32x4_t r[kPerThread];
+  __device__ __forceinline__ void load(const __bf16* head, int row0, int N) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int idx = threadIdx.x + 256 * i, row = idx / kChunks, ch = idx % kChunks;
+      r[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (row0 + row < N) r[i] = *(const u32x4_t*)(head + (size_t)(row0 + row) * D + ch * 8);
+    }
+  }
+  __device__ __forceinline__ void store(unsigned tile) const {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int idx = threadIdx.x + 256 * i, row = idx / kChunks, ch = idx % kChunks;
+      *(LDS_AS u32x4_t*)(uintptr_t)(tile + chunk_offset<D>(row, ch)) = r[i];
+    }
+  }
+};
+
+// Workgroup id -> logical tile id such that each XCD (ids w with w % 8 == x) gets
+// a contiguous range: a head's tiles share one L2.
+__device__ __forceinline__ int remap_xcd(int w, int total) {
+  const int xcd = w & 7, idx = w >> 3;
+  const int base = total >> 3, rem = total & 7;
+  return xcd < rem ? xcd * (base + 1) + idx : rem * (base + 1) + (xcd - rem) * base + idx;
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+
+// ---- kernel 1: D_i = dO_i . O_i and LSE_i * log2(e) ----
+// D/8 lanes per row (8 elements each), 64*8/D rows per wave.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dO,
+                                                      const float* __restrict__ lse, float* __restrict__ dvec,
+                                                      float* __restrict__ lse2, long long rows) {
+  constexpr int kLanes = D / 8, kRowsPerWave = 64 / kLanes;
+  const int lane = threadIdx.x & 63, t = lane % kLanes;
+  const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave + lane / kLanes;
+  float s = 0.0f;
+  if (row < rows) {
+    const u32x4_t a = *(const u32x4_t*)(o + row * D + 8 * t);
+    const u32x4_t b = *(const u32x4_t*)(dO + row * D + 8 * t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned aj = a[j], bj = b[j];
+      s = __builtin_fmaf(__builtin_bit_cast(float, aj << 16), __builtin_bit_cast(float, bj << 16), s);
+      s = __builtin_fmaf(__builtin_bit_cast(float, aj & 0xFFFF0000u), __builtin_bit_cast(float, bj & 0xFFFF0000u), s);
+    }
+  }
+  s += dpp<0xB1>(s);   // quad_perm [1,0,3,2]
+  s += dpp<0x4E>(s);   // quad_perm [2,3,0,1]
+  s += dpp<0x141>(s);  // row_half_mirror
+  if constexpr (D == 128) s += dpp<0x140>(s);  // row_mirror
+  if (row < rows && t == 0) {
+    dvec[row] = s;
+    lse2[row] = lse[row] * kLog2e;
+  }
+}
+
+// ---- kernel 2: dQ ----
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                     const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
+                                                     const float* __restrict__ dvec, const float* __restrict__ lse2,
+                                                     __bf16* __restrict__ dq, int N, int tiles_per_head,
+                                                     int total_tiles, float c, float scale) {
+  constexpr int KS = D / 16, DB = D / 32, kTile = 32 * D * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTile];  // 2 stages x (K, V)
+  const unsigned lds = (unsigned)(uintptr_t)(LDS_AS char*)smem;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+  const int logical = remap_xcd(blockIdx.x, total_tiles);
+  const int bh = logical / tiles_per_head, qt = logical % tiles_per_head;
+  const size_t head = (size_t)bh * N * D;
+  const int qrow = qt * 128 + wave * 32 + (lane & 31);
+
+  bf16x8_t qf[KS], df[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = bf16x8_t{};
+    df[ks] = bf16x8_t{};
+    if (qrow < N) {
+      qf[ks] = *(const bf16x8_t*)(q + head + (size_t)qrow * D + ks * 16 + g * 8);
+      df[ks] = *(const bf16x8_t*)(dO + head + (size_t)qrow * D + ks * 16 + g * 8);
+    }
+  }
+  const float lq = qrow < N ? lse2[(size_t)bh * N + qrow] : __builtin_inff();  // padded rows: P = 0
+  const float dd = qrow < N ? dvec[(size_t)bh * N + qrow] : 0.0f;
+  f32x16_t acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+
+  const int T = (N + 31) / 32;
+  TileCopy<D, 32> ck, cv;
+  ck.load(k + head, 0, N);
+  cv.load(v + head, 0, N);
+  ck.store(lds);
+  cv.store(lds + kTile);
+  __syncthreads();
+  for (int t = 0; t < T; ++t) {
+    const unsigned kt = lds + (t & 1) * 2 * kTile, vt = kt + kTile;
+    if (t + 1 < T) {
+      ck.load(k + head, (t + 1) * 32, N);
+      cv.load(v + head, (t + 1) * 32, N);
+    }
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma(read_row<D>(kt, ks, lane), qf[ks], s);
+      dp = mfma(read_row<D>(vt, ks, lane), df[ks], dp);
+    }
+    float ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = t * 32 + acc_row(i, g);
+      const float p = key < N ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq)) : 0.0f;
+      ds[i] = p * (dp[i] - dd);
+    }
+    const bf16x8_t b0 = pack8(ds), b1 = pack8(ds + 8);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = mfma(read_tr<D>(kt, 0, db * 32, lane), b0, acc[db]);
+      acc[db] = mfma(read_tr<D>(kt, 16, db * 32, lane), b1, acc[db]);
+    }
+    if (t + 1 < T) {
+      const unsigned nt = lds + ((t + 1) & 1) * 2 * kTile;
+      ck.store(nt);
+      cv.store(nt + kTile);
+    }
+    __syncthreads();
+  }
+  // Lane holds dQ^T rows (columns of dQ) db*32 + 8*(i/4) + 4g + i%4 of query qrow.
+  if (qrow < N) {
+    __bf16* out = dq + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x2_t a = {acc[db][4 * i4] * scale, acc[db][4 * i4 + 1] * scale};
+        const f32x2_t b = {acc[db][4 * i4 + 2] * scale, acc[db][4 * i4 + 3] * scale};
+        const u32x2_t w = {__builtin_bit_cast(unsigned, __builtin_convertvector(a, bf16x2_t)),
+                           __builtin_bit_cast(unsigned, __builtin_convertvector(b, bf16x2_t))};
+        *(u32x2_t*)(out + db * 32 + 8 * i4 + 4 * g) = w;
+      }
+    }
+  }
+}
+
+// ---- kernel 3: dK and dV ----
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                       const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
+                                                       const float* __restrict__ dvec, const float* __restrict__ lse2,
+                                                       __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N,
+                                                       int tiles_per_head, int total_tiles, float c, float scale) {
+  constexpr int KS = D / 16, DB = D / 32, kTile = 32 * D * 2;
+  constexpr int kStage = 2 * kTile + 2 * 32 * 4;  // Q tile, dO tile, LSE2[32], D[32]
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+  const unsigned lds = (unsigned)(uintptr_t)(LDS_AS char*)smem;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+  const int logical = remap_xcd(blockIdx.x, total_tiles);
+  const int bh = logical / tiles_per_head, kt0 = logical % tiles_per_head;
+  const size_t head = (size_t)bh * N * D;
+  const size_t rowvec = (size_t)bh * N;
+  const int krow = kt0 * 128 + wave * 32 + (lane & 31);
+
+  bf16x8_t kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = bf16x8_t{};
+    vf[ks] = bf16x8_t{};
+    if (krow < N) {
+      kf[ks] = *(const bf16x8_t*)(k + head + (size_t)krow * D + ks * 16 + g * 8);
+      vf[ks] = *(const bf16x8_t*)(v + head + (size_t)krow * D + ks * 16 + g * 8);
+    }
+  }
+  f32x16_t adk[DB], adv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    adk[db] = f32x16_t{};
+    adv[db] = f32x16_t{};
+  }
+
+  const int T = (N + 31) / 32;
+  TileCopy<D, 32> cq, cdo;
+  // Row vectors of the tile: thread i < 32 copies LSE2 of row i, thread 32 + i its D.
+  float vec = 0.0f;
+  auto load_vec = [&](int row0) {
+    const int i = threadIdx.x & 31, r = row0 + i;
+    if (threadIdx.x < 32) vec = r < N ? lse2[rowvec + r] : __builtin_inff();  // padded rows: P = 0
+    else if (threadIdx.x < 64) vec = r < N ? dvec[rowvec + r] : 0.0f;
+  };
+  auto store_vec = [&](unsigned st) {
+    if (threadIdx.x < 64) *(LDS_AS float*)(uintptr_t)(st + 2 * kTile + 4 * threadIdx.x) = vec;
+  };
+  cq.load(q + head, 0, N);
+  cdo.load(dO + head, 0, N);
+  load_vec(0);
+  cq.store(lds);
+  cdo.store(lds + kTile);
+  store_vec(lds);
+  __syncthreads();
+  for (int t = 0; t < T; ++t) {
+    const unsigned st = lds + (t & 1) * kStage, qtl = st, dtl = st + kTile;
+    const LDS_AS float* l2v = (const LDS_AS float*)(uintptr_t)(st + 2 * kTile);
+    const LDS_AS float* dvv = l2v + 32;
+    if (t + 1 < T) {
+      cq.load(q + head, (t + 1) * 32, N);
+      cdo.load(dO + head, (t + 1) * 32, N);
+      load_vec((t + 1) * 32);
+    }
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma(read_row<D>(qtl, ks, lane), kf[ks], s);
+      dp = mfma(read_row<D>(dtl, ks, lane), vf[ks], dp);
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int r = acc_row(4 * i4, g);  // rows r .. r+3 of the tile
+      const f32x4_t l4 = *(const LDS_AS f32x4_t*)(l2v + r);
+      const f32x4_t d4 = *(const LDS_AS f32x4_t*)(dvv + r);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * i4 + j;
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l4[j]));
+        ds[i] = p[i] * (dp[i] - d4[j]);
+      }
+    }
+    const bf16x8_t p0 = pack8(p), p1 = pack8(p + 8), s0 = pack8(ds), s1 = pack8(ds + 8);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      adv[db] = mfma(read_tr<D>(dtl, 0, db * 32, lane), p0, adv[db]);
+      adv[db] = mfma(read_tr<D>(dtl, 16, db * 32, lane), p1, adv[db]);
+      adk[db] = mfma(read_tr<D>(qtl, 0, db * 32, lane), s0, adk[db]);
+      adk[db] = mfma(read_tr<D>(qtl, 16, db * 32, lane), s1, adk[db]);
+    }
+    if (t + 1 < T) {
+      const unsigned nst = lds + ((t + 1) & 1) * kStage;
+      cq.store(nst);
+      cdo.store(nst + kTile);
+      store_vec(nst);
+    }
+    __syncthreads();
+  }
+  if (krow < N) {
+    __bf16* ok = dk + head + (size_t)krow * D;
+    __bf16* ov = dv + head + (size_t)krow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int col = db * 32 + 8 * i4 + 4 * g;
+        const f32x2_t ka = {adk[db][4 * i4] * scale, adk[db][4 * i4 + 1] * scale};
+        const f32x2_t kb = {adk[db][4 * i4 + 2] * scale, adk[db][4 * i4 + 3] * scale};
+        const f32x2_t va = {adv[db][4 * i4], adv[db][4 * i4 + 1]};
+        const f32x2_t vb = {adv[db][4 * i4 + 2], adv[db][4 * i4 + 3]};
+        *(u32x2_t*)(ok + col) = u32x2_t{__builtin_bit_cast(unsigned, __builtin_convertvector(ka, bf16x2_t)),
+                                        __builtin_bit_cast(unsigned, __builtin_convertvector(kb, bf16x2_t))};
+        *(u32x2_t*)(ov + col) = u32x2_t{__builtin_bit_cast(unsigned, __builtin_convertvector(va, bf16x2_t)),
+                                        __builtin_bit_cast(unsigned, __builtin_convertvector(vb, bf16x2_t))};
+      }
+    }
+  }
+}
+
+template <int D>
+void launch_bwd_d(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                  void* dq, void* dk, void* dv, int BH, int N, float scale, float* dvec, float* lse2, hipStream_t st) {
+  const long long rows = (long long)BH * N;
+  constexpr int kRowsPerBlock = 4 * (64 / (D / 8));
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256), 0,
+                     st, (const __bf16*)o, (const __bf16*)dO, lse, dvec, lse2, rows);
+  const int tiles = (N + 127) / 128;
+  const int total = BH * tiles;
+  const float c = scale * kLog2e;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)total), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
+                     (const __bf16*)v, (const __bf16*)dO, dvec, lse2, (__bf16*)dq, N, tiles, total, c, scale);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)total), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
+                     (const __bf16*)v, (const __bf16*)dO, dvec, lse2, (__bf16*)dk, (__bf16*)dv, N, tiles, total, c,
+                     scale);
+}
+
+}  // namespace
+
+int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+               void* dk, void* dv, int B, int H, int N, int d, float scale, void* workspace, void* stream) {
+  const int BH = B * H;
+  float* dvec = (float*)workspace;
+  float* lse2 = dvec + (size_t)BH * N;
+  hipStream_t st = (hipStream_t)stream;
+  if (d == 128) launch_bwd_d<128>(q, k, v, o, lse, dO, dq, dk, dv, BH, N, scale, dvec, lse2, st);
+  else launch_bwd_d<64>(q, k, v, o, lse, dO, dq, dk, dv, BH, N, scale, dvec, lse2, st);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace fa

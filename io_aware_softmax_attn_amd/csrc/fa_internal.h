@@ -38,6 +38,11 @@ DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d);
 int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
                   int d, float scale, void* workspace, void* stream);
 
+// Enqueue the three backward kernels; returns a fa_status code. Arguments already
+// validated; workspace holds at least fa_bwd_workspace_bytes(B, H, N).
+int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+               void* dk, void* dv, int B, int H, int N, int d, float scale, void* workspace, void* stream);
+
 // 1 if the current device is gfx950, 0 if not, negative fa_status on HIP error.
 int device_is_gfx950();
 

@@ -41,6 +41,11 @@ int launch_decode(const void*, const void*, const void*, void*, float*, int, int
   ++g_launches;
   return FA_OK;
 }
+int launch_bwd(const void*, const void*, const void*, const void*, const float*, const void*, void*, void*, void*, int,
+               int, int, int, float, void*, void*) {
+  ++g_launches;
+  return FA_OK;
+}
 int device_is_gfx950() { return g_device; }
 }  // namespace fa
 
@@ -148,6 +153,32 @@ int main() {
     EXPECT(fa_decode_fwd(q, k, v, o, lse, B, H, nq, N, d, sc, dws, dneed, nullptr) == FA_ERR_DEVICE);
     EXPECT(g_launches == before_dec + 1);
     std::free(dws);
+  }
+
+  // Backward: q k v o lse dO as inputs, dq dk dv outputs (reusing the buffers above
+  // for inputs and fresh ones for outputs), workspace 8*B*H*N bytes.
+  {
+    g_device = 1;
+    char* dq = static_cast<char*>(std::aligned_alloc(256, tb));
+    char* dk = static_cast<char*>(std::aligned_alloc(256, tb));
+    char* dv = static_cast<char*>(std::aligned_alloc(256, tb));
+    const size_t bneed = fa_bwd_workspace_bytes(B, H, N);
+    EXPECT(bneed == ((size_t)8 * B * H * N + 255) / 256 * 256);
+    char* bws = static_cast<char*>(std::aligned_alloc(256, bneed));
+    const int before_b = g_launches;
+    EXPECT(fa_bwd(q, k, v, o, lse, o, dq, dk, dv, B, H, N, d, sc, bws, bneed, nullptr) == FA_OK &&
+           g_launches == before_b + 1);
+    EXPECT(fa_bwd(q, k, v, o, lse, o, dq, dk, dq, B, H, N, d, sc, bws, bneed, nullptr) == FA_ERR_ALIAS);
+    EXPECT(fa_bwd(q, k, v, o, lse, o, dq, dk, q, B, H, N, d, sc, bws, bneed, nullptr) == FA_ERR_ALIAS);
+    EXPECT(fa_bwd(q, k, v, o, lse, nullptr, dq, dk, dv, B, H, N, d, sc, bws, bneed, nullptr) == FA_ERR_NULL);
+    EXPECT(fa_bwd(q, k, v, o, lse, o, dq, dk, dv, B, H, N, d, sc, bws, bneed - 1, nullptr) == FA_ERR_WORKSPACE);
+    EXPECT(fa_bwd(q, k, v, o, lse, o, dq, dk, dv, B, H, N, d, sc, dv, bneed, nullptr) == FA_ERR_WORKSPACE);
+    EXPECT(fa_bwd(q, k, v, o, lse, o, dq, dk, dv, B, H, N, 96, sc, bws, bneed, nullptr) == FA_ERR_HEADDIM);
+    EXPECT(g_launches == before_b + 1);
+    std::free(bws);
+    std::free(dq);
+    std::free(dk);
+    std::free(dv);
   }
 
   // Selector and strings.

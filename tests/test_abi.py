@@ -28,7 +28,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks", "fa_check_args",
               "fa_status_string", "fa_version", "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args",
-              "fa_fwd_tile_order"):
+              "fa_fwd_tile_order", "fa_bwd", "fa_bwd_workspace_bytes"):
         assert n in names
 
 
@@ -237,4 +237,35 @@ def test_tile_order_rejects_before_any_hip_call(fa):
             S["FA_ERR_SHAPE"]
     assert lib.fa_fwd_tile_order(A, 2 * A, 3 * A, A, 5 * A, 1, 1, 64, 128, 0.1, 1, None) == S["FA_ERR_ALIAS"]
     assert lib.fa_fwd_tile_order(None, None, None, None, None, 1, 1, 0, 128, 0.1, 2, None) == 0
+
+
+def test_bwd_workspace_and_argument_errors(fa):
+    S = fa.STATUS
+    lib = fa.lib
+    assert fa.fa_bwd_workspace_bytes(1, 2, 64) == 1024
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1) == 256
+    assert fa.fa_bwd_workspace_bytes(-1, 1, 1) == 0
+    P = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 8 * A, 9 * A]  # q k v o lse dO dq dk dv
+    W = 16 * A
+
+    def call(p=P, B=1, H=2, N=64, d=128, scale=0.1, ws=W, wsb=1024):
+        return lib.fa_bwd(*p, B, H, N, d, scale, ws, wsb, None)
+
+    def with_(i, x):
+        p = list(P)
+        p[i] = x
+        return p
+
+    assert call(d=96) == S["FA_ERR_HEADDIM"]
+    assert call(N=-1) == S["FA_ERR_SHAPE"]
+    assert call(p=with_(5, None)) == S["FA_ERR_NULL"]  # dO
+    assert call(p=with_(8, None)) == S["FA_ERR_NULL"]  # dv
+    assert call(p=with_(6, 7 * A + 8)) == S["FA_ERR_ALIGN"]  # dq
+    assert call(p=with_(6, A)) == S["FA_ERR_ALIAS"]  # dq is q
+    assert call(p=with_(7, 6 * A + 64)) == S["FA_ERR_ALIAS"]  # dk inside dO
+    assert call(p=with_(8, 8 * A)) == S["FA_ERR_ALIAS"]  # dv is dk
+    assert call(ws=None) == S["FA_ERR_WORKSPACE"]
+    assert call(wsb=1023) == S["FA_ERR_WORKSPACE"]
+    assert call(ws=9 * A) == S["FA_ERR_WORKSPACE"]  # overlaps dv
+    assert call(p=[None] * 9, N=0, ws=None, wsb=0) == 0  # empty: no-op
 
