@@ -8,6 +8,7 @@ in HBM before the timed region. Prints ONE JSON line.
                   [--no-cpu-baseline] [--unfused] [--launches-only]
   python bench.py --memory OUT_MD      (peak device memory, fused vs unfused)
   python bench.py --decode [--workload dec_...]   (decode-shaped forward, GB/s)
+  python bench.py --backward [--workload NAME]    (backward dQ, dK, dV, TFLOP/s)
 
 The roofline entry is measured live: per-launch HIP events recorded on the stream
 the kernel runs on, averaged over the timed region. Its ``traffic`` field comes
@@ -377,6 +378,100 @@ def decode_bench(args):
     print(json.dumps(line), flush=True)
 
 
+BWD_METRIC = "bwd attention TFLOP/s (10*B*H*N^2*d) & % of bf16 MFMA peak, B=1 H=32 N=8192 d=128"
+
+
+def backward_bench(args):
+    """Time the backward (three kernels) on a prefill workload and print one JSON line.
+    Algorithmic FLOPs: the five N x N x d products of the backward, 10*B*H*N^2*d
+    (2.5x the forward's four), whatever the kernels recompute."""
+    import torch
+
+    import attn_inputs
+    import io_aware_softmax_attn_amd as fa
+
+    w = attn_inputs.HEADLINE if args.workload is None else attn_inputs.WORKLOAD_BY_NAME[args.workload]
+    q, k, v = attn_inputs.make_workload(w)
+    g = torch.Generator().manual_seed(w.seed + 7919)
+    dO = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    qg, kg, vg, gg = (t.to(dev) for t in (q, k, v, dO))
+    o, lse = fa.forward(qg, kg, vg, scale=w.scale)
+    dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        fa.fa_bwd(qg, kg, vg, o, lse, gg, dq, dk, dv, ws, scale=w.scale, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        fa.fa_bwd(qg, kg, vg, o, lse, gg, dq, dk, dv, ws, scale=w.scale, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg_ms = sum(per_ms) / len(per_ms)
+    flops = 2.5 * w.flops
+    tf = flops / (avg_ms * 1e-3) / 1e12
+    line = {
+        "metric": BWD_METRIC,
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(max(wall * 1e3 / args.steps, avg_ms), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False, "path": "backward"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tf, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel_ms_avg": round(avg_ms, 4),
+            "kernel_ms_min": round(min(per_ms), 4),
+            "flops_per_launch": flops,
+            "executed_flops_per_launch": 3.5 * w.flops,
+        },
+    }
+    if not args.launches_only and not args.no_cpu_baseline:
+        from oracle import attention_backward_fp64
+
+        heads, t_total = 0, 0.0
+        while heads < w.B * w.H and t_total < 10.0:
+            b, h = divmod(heads, w.H)
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            args_h = [attn_inputs.bf16_to_f64(t[sl]) for t in (q, k, v, dO)]
+            t1 = time.perf_counter()
+            attention_backward_fp64(*args_h, w.scale)
+            t_total += time.perf_counter() - t1
+            heads += 1
+        line["cpu_baseline"] = {
+            "value": heads * 10.0 * w.N * w.N * w.d / t_total / 1e12,
+            "unit": "TFLOP/s",
+            "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads (all {w.N} rows each), fp64 numpy backward oracle, "
+                      f"{t_total:.1f} s",
+        }
+    print(json.dumps(line), flush=True)
+
+
 # Shapes of the device-memory comparison: (B, H, d, sequence lengths).
 MEMORY_SHAPES = ((2, 16, 128, (1024, 2048, 4096, 8192)), (4, 16, 64, (1024, 2048, 4096, 8192)))
 
@@ -474,6 +569,8 @@ def main():
     ap.add_argument("--summarize-io-sweep", metavar="DIR",
                     help="no GPU work: turn the FETCH_SIZE/WRITE_SIZE runs of the tile-order sweep under DIR "
                          "into profiles/fa_fwd_io_sweep.md (with --copy-calibration BYTES)")
+    ap.add_argument("--backward", action="store_true",
+                    help="the attention backward (dQ, dK, dV) on a prefill workload instead of the forward")
     ap.add_argument("--decode", action="store_true",
                     help="the decode-shaped forward (few queries against many keys) instead of the prefill "
                          "benchmark; also selects the decode kernels for --summarize-pmc")
@@ -508,6 +605,9 @@ def main():
 
     if args.decode:
         decode_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
 
     import torch

@@ -177,8 +177,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16* __restrict__
 }
 
 // ---- kernel 2: dQ ----
+// Two waves per SIMD (230 VGPRs at d = 128): one wave's softmax and LDS reads
+// overlap the other's products.
 template <int D>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                      const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
                                                      const float* __restrict__ dvec, const float* __restrict__ lse2,
                                                      __bf16* __restrict__ dq, int N, int tiles_per_head,
@@ -265,8 +267,10 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const __bf16* __restrict__ 
 }
 
 // ---- kernel 3: dK and dV ----
+// Two waves per SIMD at d = 64; at d = 128 the two d x 32 accumulators, K and V
+// (about 330 registers) leave room for one.
 template <int D>
-__global__ void __launch_bounds__(256) bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                        const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
                                                        const float* __restrict__ dvec, const float* __restrict__ lse2,
                                                        __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N,
