@@ -105,9 +105,11 @@ UNFUSED_KERNELS = ("unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel")
 
 
 DECODE_KERNELS = ("dec_split_kernel", "dec_merge_kernel")
+BWD_KERNELS = ("bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
+BWD_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_bwd.hip")
 
 
-def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, decode=False):
+def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, decode=False, backward=False):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel (or of the
     three unfused kernels, or of the two decode kernels, summed per launch) by what
     the same counters read for the plain copy of ``copy_bytes`` bytes in the same run."""
@@ -128,7 +130,8 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, dec
 
     def per_launch(table, counter):
         """Average KiB per launch: one kernel (fused) or the sum of the three."""
-        names = DECODE_KERNELS if decode else UNFUSED_KERNELS if unfused else ("fa_fwd_kernel",)
+        names = (DECODE_KERNELS if decode else BWD_KERNELS if backward else UNFUSED_KERNELS if unfused
+                 else ("fa_fwd_kernel",))
         total, raw = 0.0, []
         for name in names:
             vals = pick(table, counter, lambda k, n=name: n in k)
@@ -137,7 +140,7 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, dec
         per = [round(sum(r[i] for r in raw), 1) for i in range(min(len(r) for r in raw))]
         return total, per
 
-    is_copy = lambda k: "fa_fwd_kernel" not in k and "unf_" not in k and "dec_" not in k
+    is_copy = lambda k: "fa_fwd_kernel" not in k and "unf_" not in k and "dec_" not in k and "bwd_" not in k
     copy_fetch = pick(fetch, "FETCH_SIZE", is_copy)[0] * 1024.0
     copy_write = pick(write, "WRITE_SIZE", is_copy)[0] * 1024.0
     f_scale = copy_bytes / copy_fetch
@@ -148,9 +151,10 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, dec
     write_b = fa_write_kib * 1024.0 * w_scale
     rec = {
         "workload": w.name,
-        "path": "decode split+merge" if decode else "unfused-3-kernel" if unfused else "fused",
-        "kernel_source_sha256_16": kernel_source_hash(DECODE_SRC if decode else UNFUSED_SRC if unfused
-                                                      else KERNEL_SRC),
+        "path": ("decode split+merge" if decode else "backward" if backward else "unfused-3-kernel" if unfused
+                 else "fused"),
+        "kernel_source_sha256_16": kernel_source_hash(DECODE_SRC if decode else BWD_SRC if backward
+                                                      else UNFUSED_SRC if unfused else KERNEL_SRC),
         "hbm_bytes_per_launch": round(fetch_b + write_b),
         "fetch_bytes_per_launch": round(fetch_b),
         "write_bytes_per_launch": round(write_b),
@@ -162,7 +166,10 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, dec
         "fetch_kib_raw_per_launch": fa_fetch,
         "write_kib_raw_per_launch": fa_write,
     }
-    stem = "fa_decode" if decode else "fa_unfused" if unfused else "fa_fwd"
+    stem = "fa_decode" if decode else "fa_bwd" if backward else "fa_unfused" if unfused else "fa_fwd"
+    if backward:  # algorithmic bytes: read q, k, v, o, dO and lse, write dq, dk, dv
+        rec["min_hbm_bytes_per_launch"] = w.B * w.H * w.N * (16 * w.d + 4)
+        rec["ratio_to_min"] = round((fetch_b + write_b) / rec["min_hbm_bytes_per_launch"], 4)
     path = os.path.join(ROOT, "profiles", f"{stem}_{w.name}_traffic.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -233,7 +240,8 @@ def summarize_trace(stats_csv, command, workload):
     import attn_inputs
 
     rows = list(csv.DictReader(open(stats_csv)))
-    fused = any("fa_fwd_kernel" in r["Name"] for r in rows)
+    backward = any("bwd_dq_kernel" in r["Name"] for r in rows)
+    fused = not backward and any("fa_fwd_kernel" in r["Name"] for r in rows)
     decode = any("dec_split_kernel" in r["Name"] for r in rows)
     if decode:
         w = attn_inputs.DECODE_HEADLINE if workload is None else attn_inputs.DECODE_BY_NAME[workload]
@@ -247,7 +255,8 @@ def summarize_trace(stats_csv, command, workload):
     for r in rows:
         name = r["Name"]
         short = name[:60]
-        for base in ("fa_fwd_kernel", "unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel") + DECODE_KERNELS:
+        for base in ("fa_fwd_kernel", "unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel") + DECODE_KERNELS + \
+                BWD_KERNELS:
             if base in name:
                 args = re.findall(r"ILi(\d+)E(?:Li(\d+)E)?", name)
                 if args:
@@ -272,7 +281,16 @@ def summarize_trace(stats_csv, command, workload):
                       f"HBM bytes per call -> {gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.4f} of the {HBM_PEAK_GBS:.0f} GB/s "
                       f"HBM peak.",
                   f"Kernel source sha256[:16] of fa_decode.hip: {kernel_source_hash(DECODE_SRC)}."]
-    stem = "fa_fwd" if fused else "fa_decode" if decode else "fa_unfused"
+    if backward:
+        bwd = [r for r in rows if any(kname in r["Name"] for kname in BWD_KERNELS)]
+        total_s = sum(float(r["AverageNs"]) for r in bwd) * 1e-9
+        tf = 2.5 * w.flops / total_s / 1e12
+        lines += ["", f"Backward kernels (pre + dq + dkdv) at their average durations: {2.5 * w.flops:.4e} FLOP "
+                      f"(10*B*H*N^2*d) per call -> {tf:.1f} TFLOP/s, {tf / MFMA_BF16_PEAK_TFLOPS:.4f} of the "
+                      f"{MFMA_BF16_PEAK_TFLOPS} TFLOP/s bf16 MFMA peak. The forward launch in the table makes O and "
+                      f"LSE for the backward's inputs.",
+                  f"Kernel source sha256[:16] of fa_bwd.hip: {kernel_source_hash(BWD_SRC)}."]
+    stem = "fa_fwd" if fused else "fa_decode" if decode else "fa_bwd" if backward else "fa_unfused"
     path = os.path.join(ROOT, "profiles", f"{stem}_{w.name}_kernel_trace.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -581,7 +599,7 @@ def main():
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_calibration,
-                      unfused=args.unfused, decode=args.decode)
+                      unfused=args.unfused, decode=args.decode, backward=args.backward)
         return
     if args.summarize_io_sweep:
         summarize_io_sweep(args.summarize_io_sweep, args.copy_calibration)
