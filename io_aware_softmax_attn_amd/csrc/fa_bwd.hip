@@ -74,6 +74,30 @@ __device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b, c
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// MFMAs with pinned register classes for the dK/dV kernel, whose two d x 32
+// accumulators stay in AGPRs for the whole kernel and whose K and V operands sit in
+// AGPRs as B sources. The compiler does not see these as MFMAs, so the kernel keeps
+// the wait states itself: VALU code reads S and dP only after an s_nop pin that
+// follows the products writing them, the packed P and dS get an s_nop before the
+// products that read them, and the accumulators get sync_acc before VALU reads.
+__device__ __forceinline__ void mfma_sv(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_sv0(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_acc(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// Wait states between the last MFMA writing a VGPR result and VALU reads of it.
+__device__ __forceinline__ void sync_sv(f32x16_t& a, f32x16_t& b) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(a), "+v"(b));
+}
+// ... and between the last MFMA writing an AGPR accumulator and VALU reads of it.
+__device__ __forceinline__ void sync_acc(f32x16_t& a, f32x16_t& b) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(a), "+a"(b));
+}
+
 // Eight accumulator values -> one bf16x8 operand (nearest-even), element order kept.
 __device__ __forceinline__ bf16x8_t pack8(const float* x) {
   const bf16x2_t p0 = __builtin_convertvector((f32x2_t){x[0], x[1]}, bf16x2_t);
@@ -277,7 +301,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
                                                        int tiles_per_head, int total_tiles, float c, float scale) {
   constexpr int KS = D / 16, DB = D / 32, kTile = 32 * D * 2;
   constexpr int kStage = 2 * kTile + 2 * 32 * 4;  // Q tile, dO tile, LSE2[32], D[32]
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[3 * kStage];
   const unsigned lds = (unsigned)(uintptr_t)(LDS_AS char*)smem;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
   const int logical = remap_xcd(blockIdx.x, total_tiles);
@@ -296,6 +320,10 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
       vf[ks] = *(const bf16x8_t*)(v + head + (size_t)krow * D + ks * 16 + g * 8);
     }
   }
+  // K and V into AGPRs, with the wait states before the first MFMA that reads them.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("s_nop 1" : "+a"(kf[ks]), "+a"(vf[ks]));
+  asm volatile("s_nop 7" ::: "memory");
   f32x16_t adk[DB], adv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -307,65 +335,126 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
   TileCopy<D, 32> cq, cdo;
   // Row vectors of the tile: thread i < 32 copies LSE2 of row i, thread 32 + i its D.
   float vec = 0.0f;
-  auto load_vec = [&](int row0) {
+  auto load_tile = [&](int row0) {
+    cq.load(q + head, row0, N);
+    cdo.load(dO + head, row0, N);
     const int i = threadIdx.x & 31, r = row0 + i;
     if (threadIdx.x < 32) vec = r < N ? lse2[rowvec + r] : __builtin_inff();  // padded rows: P = 0
     else if (threadIdx.x < 64) vec = r < N ? dvec[rowvec + r] : 0.0f;
   };
-  auto store_vec = [&](unsigned st) {
+  auto store_tile = [&](unsigned st) {
+    cq.store(st);
+    cdo.store(st + kTile);
     if (threadIdx.x < 64) *(LDS_AS float*)(uintptr_t)(st + 2 * kTile + 4 * threadIdx.x) = vec;
   };
-  cq.load(q + head, 0, N);
-  cdo.load(dO + head, 0, N);
-  load_vec(0);
-  cq.store(lds);
-  cdo.store(lds + kTile);
-  store_vec(lds);
+  // S and dP of the tile at st: KS products each, in ks order. The row operands
+  // are read one step ahead: loads do not move across the asm MFMAs, so reading
+  // them right before their product would expose the LDS latency.
+  auto sdp_step = [&](int ks, const bf16x8_t& aq, const bf16x8_t& ad, f32x16_t& s, f32x16_t& dp) {
+    if (ks == 0) {
+      mfma_sv0(s, aq, kf[ks]);
+      mfma_sv0(dp, ad, vf[ks]);
+    } else {
+      mfma_sv(s, aq, kf[ks]);
+      mfma_sv(dp, ad, vf[ks]);
+    }
+  };
+  // Three stages: while tile t's softmax runs on the VALU, the matrix cores compute
+  // S and dP of tile t+1, and tile t+2 is in flight from memory. The softmax is cut
+  // into four parts placed between the product pairs, each pinned to its place
+  // (inputs at its start, outputs at its end) so the VALU work interleaves with the
+  // MFMAs instead of running before them. Tiles past the end are zero rows with
+  // LSE2 = +inf (P = 0), so every step runs the same code.
+  unsigned cur = lds, nxt = lds + kStage, fut = lds + 2 * kStage;
+  load_tile(0);
+  store_tile(cur);
+  load_tile(32);
+  store_tile(nxt);
   __syncthreads();
+  f32x16_t s, dp;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    sdp_step(ks, read_row<D>(cur, ks, lane), read_row<D>(cur + kTile, ks, lane), s, dp);
+  sync_sv(s, dp);
   for (int t = 0; t < T; ++t) {
-    const unsigned st = lds + (t & 1) * kStage, qtl = st, dtl = st + kTile;
-    const LDS_AS float* l2v = (const LDS_AS float*)(uintptr_t)(st + 2 * kTile);
+    load_tile((t + 2) * 32);
+    const LDS_AS float* l2v = (const LDS_AS float*)(uintptr_t)(cur + 2 * kTile);
     const LDS_AS float* dvv = l2v + 32;
-    if (t + 1 < T) {
-      cq.load(q + head, (t + 1) * 32, N);
-      cdo.load(dO + head, (t + 1) * 32, N);
-      load_vec((t + 1) * 32);
-    }
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma(read_row<D>(qtl, ks, lane), kf[ks], s);
-      dp = mfma(read_row<D>(dtl, ks, lane), vf[ks], dp);
-    }
     float p[16], ds[16];
+    f32x16_t s2, dp2;
+    bf16x8_t rq[KS], rd[KS];  // row operands of tile t+1; only a window is live at once
+    constexpr int kPer = KS / 4;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int r = acc_row(4 * i4, g);  // rows r .. r+3 of the tile
+    for (int ks = 0; ks < kPer; ++ks) {
+      rq[ks] = read_row<D>(nxt, ks, lane);
+      rd[ks] = read_row<D>(nxt + kTile, ks, lane);
+    }
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      if (part + 1 < 4) {
+#pragma unroll
+        for (int ks = (part + 1) * kPer; ks < (part + 2) * kPer; ++ks) {
+          rq[ks] = read_row<D>(nxt, ks, lane);
+          rd[ks] = read_row<D>(nxt + kTile, ks, lane);
+        }
+      }
+#pragma unroll
+      for (int ks = part * kPer; ks < (part + 1) * kPer; ++ks) sdp_step(ks, rq[ks], rd[ks], s2, dp2);
+      // Softmax of rows acc_row(4*part, g) .. +3 of tile t.
+      const int r = acc_row(4 * part, g);
       const f32x4_t l4 = *(const LDS_AS f32x4_t*)(l2v + r);
       const f32x4_t d4 = *(const LDS_AS f32x4_t*)(dvv + r);
+      float sx[4], dx[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int i = 4 * i4 + j;
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l4[j]));
-        ds[i] = p[i] * (dp[i] - d4[j]);
+        sx[j] = s[4 * part + j];
+        dx[j] = dp[4 * part + j];
       }
+      asm volatile("" : "+v"(sx[0]), "+v"(sx[1]), "+v"(sx[2]), "+v"(sx[3]), "+v"(dx[0]), "+v"(dx[1]), "+v"(dx[2]),
+                   "+v"(dx[3]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * part + j;
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[j], c, -l4[j]));
+        ds[i] = p[i] * (dx[j] - d4[j]);
+      }
+      asm volatile("" : "+v"(p[4 * part]), "+v"(p[4 * part + 1]), "+v"(p[4 * part + 2]), "+v"(p[4 * part + 3]),
+                   "+v"(ds[4 * part]), "+v"(ds[4 * part + 1]), "+v"(ds[4 * part + 2]), "+v"(ds[4 * part + 3]));
     }
-    const bf16x8_t p0 = pack8(p), p1 = pack8(p + 8), s0 = pack8(ds), s1 = pack8(ds + 8);
+    // Transposed operands of the accumulator products, read one column block ahead.
+    bf16x8_t tr[DB][4];
+    auto read_block = [&](int db) {
+      tr[db][0] = read_tr<D>(cur + kTile, 0, db * 32, lane);
+      tr[db][1] = read_tr<D>(cur + kTile, 16, db * 32, lane);
+      tr[db][2] = read_tr<D>(cur, 0, db * 32, lane);
+      tr[db][3] = read_tr<D>(cur, 16, db * 32, lane);
+    };
+    read_block(0);
+    bf16x8_t p0 = pack8(p), p1 = pack8(p + 8), s0 = pack8(ds), s1 = pack8(ds + 8);
+    // Two wait states between the VALU writes of the operands and the MFMAs reading them.
+    asm volatile("s_nop 1" : "+v"(p0), "+v"(p1), "+v"(s0), "+v"(s1));
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      adv[db] = mfma(read_tr<D>(dtl, 0, db * 32, lane), p0, adv[db]);
-      adv[db] = mfma(read_tr<D>(dtl, 16, db * 32, lane), p1, adv[db]);
-      adk[db] = mfma(read_tr<D>(qtl, 0, db * 32, lane), s0, adk[db]);
-      adk[db] = mfma(read_tr<D>(qtl, 16, db * 32, lane), s1, adk[db]);
+      if (db + 1 < DB) read_block(db + 1);
+      mfma_acc(adv[db], tr[db][0], p0);
+      mfma_acc(adv[db], tr[db][1], p1);
+      mfma_acc(adk[db], tr[db][2], s0);
+      mfma_acc(adk[db], tr[db][3], s1);
     }
-    if (t + 1 < T) {
-      const unsigned nst = lds + ((t + 1) & 1) * kStage;
-      cq.store(nst);
-      cdo.store(nst + kTile);
-      store_vec(nst);
-    }
+    store_tile(fut);
     __syncthreads();
+    // The products of S2 and dP2 were issued before the 4*DB accumulator products;
+    // the pin still covers the wait states before the VALU reads them.
+    sync_sv(s2, dp2);
+    s = s2;
+    dp = dp2;
+    const unsigned done = cur;
+    cur = nxt;
+    nxt = fut;
+    fut = done;
   }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) sync_acc(adk[db], adv[db]);
   if (krow < N) {
     __bf16* ok = dk + head + (size_t)krow * D;
     __bf16* ov = dv + head + (size_t)krow * D;
