@@ -180,8 +180,13 @@ IO_SWEEP_ORDERS = (0, 1, 2)
 IO_SWEEP_LENGTHS = (2048, 4096, 8192, 16384)
 IO_SWEEP_SHAPE = (1, 32, 128)  # B, H, d
 IO_SWEEP_CMD = ("rocprofv3 --pmc {ctr} -d {dir}/pmc_o{order}_n{n}_{ctr} -o c --output-format csv -- "
-                "python3 bench.py --shape {B},{H},{n},{d} --tile-order {order} --steps 2 --warmup 1 "
+                "python3 bench.py --shape {B},{H},{n},{d} --tile-order {order} --br 256 --steps 2 --warmup 1 "
                 "--launches-only --copy-calibration 1073741824")
+# The 128-row query tile (fa_fwd_blocks), XCD-aware order: twice the query tiles per
+# head, so twice the K/V passes that the on-chip caches must absorb.
+IO_SWEEP_BR_CMD = ("rocprofv3 --pmc {ctr} -d {dir}/pmc_b128_n{n}_{ctr} -o c --output-format csv -- "
+                   "python3 bench.py --shape {B},{H},{n},{d} --br 128 --steps 2 --warmup 1 "
+                   "--launches-only --copy-calibration 1073741824")
 
 
 def summarize_io_sweep(sweep_dir, copy_bytes):
@@ -190,41 +195,48 @@ def summarize_io_sweep(sweep_dir, copy_bytes):
     profiles/fa_fwd_io_sweep.md next to two models: every byte once, and every
     query tile re-reading its head's K and V."""
     B, H, d = IO_SWEEP_SHAPE
-    names = {0: "XCD-aware (fa_fwd)", 1: "dispatch order", 2: "query-tile-major"}
+    names = {0: "XCD-aware", 1: "dispatch order", 2: "query-tile-major"}
     rows = []
-    for order in IO_SWEEP_ORDERS:
+    runs = [(order, 256, f"pmc_o{order}_n{{n}}") for order in IO_SWEEP_ORDERS]
+    if os.path.isdir(os.path.join(sweep_dir, f"pmc_b128_n{IO_SWEEP_LENGTHS[0]}_FETCH_SIZE")):
+        runs.append((0, 128, "pmc_b128_n{n}"))
+    for order, br, stem in runs:
         for n in IO_SWEEP_LENGTHS:
             vals = {}
             for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
-                table = _read_counter_csv(os.path.join(sweep_dir, f"pmc_o{order}_n{n}_{ctr}", "c_counter_collection.csv"))
+                table = _read_counter_csv(os.path.join(sweep_dir, stem.format(n=n) + f"_{ctr}",
+                                                       "c_counter_collection.csv"))
                 fa_vals = [v for (kname, c), vs in table.items() if c == ctr and "fa_fwd_kernel" in kname for v in vs]
                 copy = [v for (kname, c), vs in table.items() if c == ctr and "fa_fwd_kernel" not in kname for v in vs]
                 vals[ctr] = sum(fa_vals) / len(fa_vals) * copy_bytes / copy[0]
             total = vals["FETCH_SIZE"] + vals["WRITE_SIZE"]
             minimum = B * H * n * (8 * d + 4)
-            tiles = -(-n // 256)
+            tiles = -(-n // br)
             reread = B * H * (tiles * 4 * n * d + n * (4 * d + 4))  # K, V per query tile; Q, O, LSE once
-            rows.append((order, n, total, minimum, reread))
+            rows.append((order, br, n, total, minimum, reread))
     lines = [
         "# Fused-kernel HBM traffic by workgroup-to-tile order and sequence length",
         "",
-        f"B={B} H={H} d={d}, 256 query rows per workgroup. Bytes per launch from FETCH_SIZE + WRITE_SIZE "
-        "(KiB per dispatch), each scaled by what the counter reads for a 1 GiB device-to-device copy in the "
-        "same run, averaged over the 3 launches of each run. One run per order, length and counter:",
+        f"B={B} H={H} d={d}; BR query rows per workgroup (256 unless stated). Bytes per launch from "
+        "FETCH_SIZE + WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads for a 1 GiB "
+        "device-to-device copy in the same run, averaged over the 3 launches of each run. One run per order "
+        "(or BR), length and counter:",
         "",
         "```",
         IO_SWEEP_CMD.format(ctr="<FETCH_SIZE|WRITE_SIZE>", dir="gpurun_out/io_sweep", order="<order>", n="<N>",
                             B=B, H=H, d=d),
+        IO_SWEEP_BR_CMD.format(ctr="<FETCH_SIZE|WRITE_SIZE>", dir="gpurun_out/io_sweep", n="<N>", B=B, H=H, d=d),
         "```",
         "",
         "Models: `once` = B*H*N*(8d+4) (Q, K, V read once, O and LSE written once); `re-read` = K and V "
-        "read again by every query tile of their head, ceil(N/256) times, plus Q, O, LSE once.",
+        "read again by every query tile of their head, ceil(N/BR) times, plus Q, O, LSE once.",
         "",
-        "| order | N | bytes per launch | / once | / re-read |",
-        "|---|---|---|---|---|",
+        "| order | BR | N | bytes per launch | / once | / re-read |",
+        "|---|---|---|---|---|---|",
     ]
-    for order, n, total, minimum, reread in rows:
-        lines.append(f"| {order} {names[order]} | {n} | {total:,.0f} | {total / minimum:.3f} | {total / reread:.3f} |")
+    for order, br, n, total, minimum, reread in rows:
+        lines.append(f"| {order} {names[order]} | {br} | {n} | {total:,.0f} | {total / minimum:.3f} | "
+                     f"{total / reread:.3f} |")
     lines += ["", f"Kernel source sha256[:16] of fa_fwd.hip: {kernel_source_hash()}."]
     path = os.path.join(ROOT, "profiles", "fa_fwd_io_sweep.md")
     with open(path, "w") as f:
@@ -582,6 +594,8 @@ def main():
                          "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin")
     ap.add_argument("--tile-order", type=int, default=0, choices=(0, 1, 2),
                     help="fused path only: workgroup-to-tile order of fa_fwd_tile_order (0 = fa_fwd's)")
+    ap.add_argument("--br", type=int, default=0, choices=(0, 128, 256),
+                    help="fused path only: query rows per workgroup (fa_fwd_blocks); 0 = the selector's choice")
     ap.add_argument("--shape", metavar="B,H,N,d",
                     help="a fused-path shape outside the named workloads (seed 0, unit Gaussian inputs)")
     ap.add_argument("--summarize-io-sweep", metavar="DIR",
@@ -660,6 +674,8 @@ def main():
             fa.fa_unfused_fwd(qg, kg, vg, o, lse, ws, scale=w.scale, stream=stream)
         elif args.tile_order:
             fa.fa_fwd_tile_order(qg, kg, vg, o, lse, args.tile_order, scale=w.scale, stream=stream)
+        elif args.br:
+            fa.fa_fwd_blocks(qg, kg, vg, o, lse, args.br, scale=w.scale, stream=stream)
         else:
             fa.fa_fwd(qg, kg, vg, o, lse, scale=w.scale, stream=stream)
 
@@ -681,7 +697,7 @@ def main():
     step_ms = max(wall * 1e3 / args.steps, avg_ms)
 
     tflops = w.flops / (avg_ms * 1e-3) / 1e12
-    traffic = None if args.unfused else load_traffic(w.name)
+    traffic = None if (args.unfused or args.br or args.tile_order) else load_traffic(w.name)
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -697,6 +713,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False,
                    "path": "unfused-3-kernel" if args.unfused else "fused",
+                   **({} if args.unfused else {"br": args.br or fa.fa_select_blocks(w.d, w.N, w.B, w.H)[0]}),
                    **({"tile_order": args.tile_order} if args.tile_order else {})},
         "roofline": {
             "bound": "mfma",

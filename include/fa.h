@@ -89,6 +89,19 @@ int fa_fwd_tile_order(const void* q, const void* k, const void* v, void* o, floa
                       int B, int H, int N, int d, float scale, int order, void* stream);
 
 /*
+ * fa_fwd with an explicit query-tile height br (rows of Q per workgroup): 256 or
+ * 128, the two compiled shapes (4 waves of 64 or 32 rows, 64-key K/V tiles). The
+ * pages size the query tile against on-chip memory ("01 · 注意力为什么是 IO 瓶颈",
+ * section 7) and count the K/V traffic as one pass per query tile (same section);
+ * this entry point lets a caller compare the two heights. Results for a given
+ * br are bitwise deterministic; the two heights may differ in the last bits, as
+ * a wave decides when to move its softmax reference over its own rows. Returns
+ * FA_ERR_SHAPE for any other br; otherwise as fa_fwd.
+ */
+int fa_fwd_blocks(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int N, int d, float scale, int br, void* stream);
+
+/*
  * The textbook three-step forward ("01 · 注意力为什么是 IO 瓶颈", section 3
  * table and section 5): kernel 1 writes S = scale*QK^T (fp32, [B,H,N,Ns]) to the
  * workspace, kernel 2 reads S and writes P = softmax(S) (bf16, [B,H,N,Ns]) and
@@ -108,8 +121,12 @@ size_t fa_unfused_workspace_bytes(int B, int H, int N);
 /*
  * Block-size selector: the (query rows per workgroup, keys per tile, waves per
  * workgroup) the fused kernel uses for this shape ("01 ·" page, section 7: tiles
- * are sized against on-chip memory). Writes *br, *bc, *nwaves; returns FA_OK,
- * FA_ERR_NULL or FA_ERR_HEADDIM.
+ * are sized against on-chip memory; kp-015 page, "常见误区": the gain depends on
+ * the number of compute units). br is 256 or 128, bc is 64, nwaves is 4; the
+ * choice depends on the shape only (d, N, B*H against the 256 compute units of
+ * the part), never on the device the call runs on, so results stay a function
+ * of the shape. Writes *br, *bc, *nwaves; returns FA_OK, FA_ERR_NULL,
+ * FA_ERR_SHAPE (B, H or N negative) or FA_ERR_HEADDIM.
  */
 int fa_select_blocks(int d, int N, int B, int H, int* br, int* bc, int* nwaves);
 

@@ -21,7 +21,7 @@ __all__ = [
     "FaError", "lib", "fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks",
     "fa_check_args", "fa_status_string", "fa_version", "forward", "unfused_forward",
     "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args", "decode_forward", "DECODE_MAX_NQ",
-    "fa_fwd_tile_order", "TILE_ORDERS", "fa_bwd", "fa_bwd_workspace_bytes", "backward",
+    "fa_fwd_tile_order", "TILE_ORDERS", "fa_fwd_blocks", "fa_bwd", "fa_bwd_workspace_bytes", "backward",
     "STATUS",
 ]
 
@@ -69,6 +69,8 @@ def _load() -> ctypes.CDLL:
     dll.fa_bwd_workspace_bytes.restype = sz
     dll.fa_fwd_tile_order.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     dll.fa_fwd_tile_order.restype = i
+    dll.fa_fwd_blocks.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    dll.fa_fwd_blocks.restype = i
     dll.fa_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp]
     dll.fa_decode_fwd.restype = i
     dll.fa_decode_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(sz)]
@@ -180,6 +182,18 @@ def fa_fwd_tile_order(q, k, v, o, lse, order, scale=None, stream=None):
     with torch.cuda.device(q.device):
         _raise(lib.fa_fwd_tile_order(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                                      int(order), _stream_handle(stream, q.device)), "fa_fwd_tile_order")
+    return o, lse
+
+
+def fa_fwd_blocks(q, k, v, o, lse, br, scale=None, stream=None):
+    """fa_fwd with an explicit query-tile height ``br`` (256 or 128 rows per workgroup)
+    instead of the selector's choice."""
+    B, H, N, d = _shape_of(q, k, v, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(q.device):
+        _raise(lib.fa_fwd_blocks(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                 int(br), _stream_handle(stream, q.device)), "fa_fwd_blocks")
     return o, lse
 
 

@@ -65,6 +65,7 @@ size_t fa_unfused_workspace_bytes(int B, int H, int N) {
 int fa_select_blocks(int d, int N, int B, int H, int* br, int* bc, int* nwaves) {
   if (!br || !bc || !nwaves) return FA_ERR_NULL;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   const fa::Blocks b = fa::select_blocks(d, N, B, H);
   *br = b.br;
   *bc = b.bc;
@@ -86,8 +87,8 @@ int fa_check_args(const void* q, const void* k, const void* v, const void* o, co
   uint64_t elems, tbytes, lbytes;
   if (!mul_ok(rows64, (uint64_t)d, &elems) || !mul_ok(elems, 2, &tbytes) || !mul_ok(rows64, 4, &lbytes))
     return FA_ERR_OVERFLOW;
-  // Launch grid: one workgroup per (b, h, query tile of the widest block, 256 rows).
-  const uint64_t tiles = ((uint64_t)N + 255) / 256;
+  // Launch grid: one workgroup per (b, h, query tile); the narrowest tile has 128 rows.
+  const uint64_t tiles = ((uint64_t)N + 127) / 128;
   if ((uint64_t)B * (uint64_t)H * tiles > (uint64_t)std::numeric_limits<int32_t>::max()) return FA_ERR_OVERFLOW;
   auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
@@ -242,6 +243,20 @@ int fa_fwd_tile_order(const void* q, const void* k, const void* v, void* o, floa
   if (dev < 0) return dev;
   if (dev == 0) return FA_ERR_DEVICE;
   return fa::launch_fused(q, k, v, o, lse, B, H, N, d, scale, fa::select_blocks(d, N, B, H), stream, order);
+}
+
+int fa_fwd_blocks(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                  float scale, int br, void* stream) {
+  if (br != 128 && br != 256) return FA_ERR_SHAPE;
+  const int st = fa_check_args(q, k, v, o, lse, B, H, N, d, scale, 0, nullptr, 0);
+  if (st != FA_OK) return st;
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)N == 0) return FA_OK;
+  const int dev = fa::device_is_gfx950();
+  if (dev < 0) return dev;
+  if (dev == 0) return FA_ERR_DEVICE;
+  fa::Blocks blk = fa::select_blocks(d, N, B, H);
+  blk.br = br;
+  return fa::launch_fused(q, k, v, o, lse, B, H, N, d, scale, blk, stream);
 }
 
 int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,

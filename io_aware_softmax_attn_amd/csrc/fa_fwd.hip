@@ -57,11 +57,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// K/V tiling, common to both query-tile heights. A wave owns NQB blocks of 32
+// query rows (NQB = 2: BR = 256 rows per workgroup; NQB = 1: BR = 128).
 template <int D>
 struct Cfg {
   static constexpr int kWaves = 4;
-  static constexpr int kRowsPerWave = 64;
-  static constexpr int kBR = kWaves * kRowsPerWave;
   static constexpr int kBC = 64;
   static constexpr int kStages = 4;     // K/V tiles resident in LDS
   static constexpr int kAhead = kStages - 2;  // tiles loading while the current one is read
@@ -268,6 +268,18 @@ __device__ __forceinline__ void mfma_rowsum(f32x4_t& d, bf16x8_t& sel, const bf1
 __device__ __forceinline__ void sync_acc(f32x16_t& a, f32x16_t& b) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(a), "+a"(b));
 }
+__device__ __forceinline__ void sync_acc(f32x16_t& a) { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(a)); }
+template <int DB, int NQB>
+__device__ __forceinline__ void sync_acc_all(f32x16_t (&acc)[DB][NQB]) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    if constexpr (NQB == 2) {
+      sync_acc(acc[db][0], acc[db][1]);
+    } else {
+      sync_acc(acc[db][0]);
+    }
+  }
+}
 
 // Key index, within a 32-key sub-tile, of S^T accumulator register i, minus 8g:
 // key = 8g + 16*(i/8) + 4*((i/4)%2) + i%4 (the pi row permutation).
@@ -281,35 +293,35 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// State of one wave's 64 query rows (two 32-row MFMA column blocks qb = 0, 1).
-template <int D>
+// State of one wave's 32*NQB query rows (32-row MFMA column blocks qb < NQB).
+template <int D, int NQB>
 struct Wave {
   using C = Cfg<D>;
-  bf16x8_t qf[2][C::kKS];     // Q^T operands (AGPRs)
+  bf16x8_t qf[NQB][C::kKS];   // Q^T operands (AGPRs)
   unsigned koff[C::kKS];      // LDS addresses of this lane's K operand reads (stage 0, sub-tile 0)
   unsigned voff[C::kDB][2];   // ... and of its V transposing reads (tile base excluded)
   unsigned koff2[C::kKS];     // the same plus 64 KiB: bases for sub-tiles whose offset exceeds
   unsigned voff2[C::kDB][2];  // the 16-bit immediate of ds_read
   unsigned gofs[C::kLoadsPerWave];  // this lane's tile_load_offset values
-  f32x16_t acc[C::kDB][2];    // O^T accumulator (AGPRs)
-  float m[2];                 // reference max, log2 units
-  float l[2];                 // this lane's part of the running sum of the exp2 terms (for LSE)
-  f32x4_t lbacc[2];           // row sums of the bf16 terms that entered the PV product (for O)
+  f32x16_t acc[C::kDB][NQB];  // O^T accumulator (AGPRs)
+  float m[NQB];               // reference max, log2 units
+  float l[NQB];               // this lane's part of the running sum of the exp2 terms (for LSE)
+  f32x4_t lbacc[NQB];         // row sums of the bf16 terms that entered the PV product (for O)
   bf16x8_t sel;               // the 0/1 selector operand of mfma_rowsum
   bf16x8_t vpre[4];           // V^T operands of the next step's first PV slots, read ahead
   bool rescale;               // the reference max moved in the last softmax: scale acc
-  float alpha[2];             // ... by exp2(m_old - m_new) before the next PV product
+  float alpha[NQB];           // ... by exp2(m_old - m_new) before the next PV product
 };
 
 // Online-softmax reference update for one 32-key sub-tile (FA1 page, derivation
 // steps 1-2), the slow path: the row max of the sub-tile, a new reference max
 // m_new = max(m, rowmax) per row, alpha = exp2(m_old - m_new), and l rescaled.
 // kMasked sets keys >= nvalid (passed as nvalid - 8g) to -inf first.
-template <bool kMasked>
-__device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], float (&l)[2], float (&alpha)[2],
-                                               float c, int nv8) {
+template <bool kMasked, int NQB>
+__device__ __forceinline__ void move_reference(f32x16_t (&s)[NQB], float (&m)[NQB], float (&l)[NQB],
+                                               float (&alpha)[NQB], float c, int nv8) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     float x = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -347,16 +359,16 @@ __device__ __forceinline__ void move_reference(f32x16_t (&s)[2], float (&m)[2], 
 // those of j are read). kMasked: sub-tile j is the ragged last one (keys >= nvalid,
 // passed as nvalid - 8g, are masked). kJP >= 0: j mod the ring period (2 * kStages)
 // is known at compile time.
-template <int D, bool kPV, bool kExp, bool kQK, bool kMasked, int kJP>
-__device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, const char* gk, const char* gv,
-                                              LDS_AS char* lds, int wave, int lane, f32x16_t (&scur)[2],
-                                              f32x16_t (&snxt)[2], const bf16x8_t (&pprev)[2][2],
-                                              bf16x8_t (&pcur)[2][2], float c, int nv8) {
+template <int D, int NQB, bool kPV, bool kExp, bool kQK, bool kMasked, int kJP>
+__device__ __forceinline__ void pipeline_step(Wave<D, NQB>& w, int j, int T, int N, const char* gk, const char* gv,
+                                              LDS_AS char* lds, int wave, int lane, f32x16_t (&scur)[NQB],
+                                              f32x16_t (&snxt)[NQB], const bf16x8_t (&pprev)[NQB][2],
+                                              bf16x8_t (&pcur)[NQB][2], float c, int nv8) {
   using C = Cfg<D>;
   constexpr int KS = C::kKS, DB = C::kDB;
-  constexpr int NPV = kPV ? 4 * DB : 0;        // MFMA slots of the PV product (first)
-  constexpr int NS = NPV + (kQK ? 2 * KS : 0);  // all MFMA slots
-  constexpr int NE = 32;                       // score registers per lane (2 blocks x 16)
+  constexpr int NPV = kPV ? 2 * DB * NQB : 0;     // MFMA slots of the PV product (first)
+  constexpr int NS = NPV + (kQK ? KS * NQB : 0);  // all MFMA slots
+  constexpr int NE = 16 * NQB;                    // score registers per lane (NQB blocks x 16)
   // The softmax is staged over the NS MFMA slots: NAS slots issue fma work, exp2
   // and packing trail by one and two slots. Each PV slot whose d-block is 1 is
   // followed by a row-sum MFMA of the same P^T operand (16x16x32, half as long),
@@ -369,7 +381,10 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   constexpr int NPAIR = 2 * DB;                // V^T operand pairs (h, db) of a PV product
   constexpr int kVPre = 4;                     // pairs read in the previous step
   constexpr int kVLead = 4;                    // other pairs: read this many pairs ahead
-  constexpr int kKStart = NPV > 8 ? NPV - 8 : 0;  // slot where K operand reads start
+  // K operand reads run four k-steps (4 * NQB slots) ahead of their MFMA, starting
+  // kKStart slots in; with fewer PV slots, three are read before the first slot.
+  constexpr int kKLead = 4 * NQB;
+  constexpr int kKStart = NPV > kKLead ? NPV - kKLead : 0;
   constexpr float kSumLimit = 65536.0f;
   static_assert(NPAIR >= kVPre, "prefetch depth");
 
@@ -377,26 +392,33 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     // The previous softmax moved the reference max (uniform branch, rarely
     // taken): bring the PV products accumulated so far to the new reference.
     if (w.rescale) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
+      sync_acc_all(w.acc);
       // One fragment at a time: each asm ties the finished fragment to the next
-      // one, so the compiler cannot pull all 128 values into VGPRs at once.
+      // one, so the compiler cannot pull all of them into VGPRs at once.
 #pragma unroll
-      for (int f = 0; f < 2 * DB; ++f) {
-        w.acc[f >> 1][f & 1] *= w.alpha[f & 1];
-        if (f + 1 < 2 * DB) asm volatile("" : "+a"(w.acc[f >> 1][f & 1]), "+a"(w.acc[(f + 1) >> 1][(f + 1) & 1]));
+      for (int f = 0; f < NQB * DB; ++f) {
+        w.acc[f / NQB][f % NQB] *= w.alpha[f % NQB];
+        if (f + 1 < NQB * DB)
+          asm volatile("" : "+a"(w.acc[f / NQB][f % NQB]), "+a"(w.acc[(f + 1) / NQB][(f + 1) % NQB]));
       }
       // The row-sum MFMAs of the previous step finished during sync_acc's wait; the
       // empty asm keeps the reads below after it. Lane l's row sum belongs to query
       // (l%16) + 16*(l/32) (see mfma_rowsum), whose alpha sits in lane (that query).
-      asm volatile("" : "+v"(w.lbacc[0]), "+v"(w.lbacc[1]));
+      if constexpr (NQB == 2) {
+        asm volatile("" : "+v"(w.lbacc[0]), "+v"(w.lbacc[1]));
+      } else {
+        asm volatile("" : "+v"(w.lbacc[0]));
+      }
       const int src = ((lane & 15) | ((lane >> 5) << 4)) * 4;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < NQB; ++qb)
         w.lbacc[qb] *= __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, w.alpha[qb])));
-      asm volatile("s_nop 1" : "+v"(w.lbacc[0]), "+v"(w.lbacc[1]));
-#pragma unroll
-      for (int db = 0; db < DB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
+      if constexpr (NQB == 2) {
+        asm volatile("s_nop 1" : "+v"(w.lbacc[0]), "+v"(w.lbacc[1]));
+      } else {
+        asm volatile("s_nop 1" : "+v"(w.lbacc[0]));
+      }
+      sync_acc_all(w.acc);
       w.rescale = false;
     }
   }
@@ -502,9 +524,9 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   // ---- softmax of sub-tile j, staged: fma (A), exp2 (B), sum + pack (C) ----
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  float tv[2][16];
-  float sum[2][2];  // per-lane partial sums of the terms, even and odd registers
-  unsigned pk[2][8];  // packed bf16 pairs, assembled into pcur per 8-key operand
+  float tv[NQB][16];
+  float sum[NQB][2];  // per-lane partial sums of the terms, even and odd registers
+  unsigned pk[NQB][8];  // packed bf16 pairs, assembled into pcur per 8-key operand
   auto stage_a = [&](auto e_tag) {
     constexpr int e = decltype(e_tag)::value, qb = e / 16, i = e % 16;
     tv[qb][i] = __builtin_fmaf(scur[qb][i], c, -w.m[qb]);
@@ -554,11 +576,17 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
         // before the previous step's last MFMA has run its 32 cycles, so the MFMAs
         // that wrote scur (issued before that one) have finished. The s_nop adds the
         // two wait states of a VALU read after an MFMA issue.
-        asm volatile("s_nop 1" : "+v"(sw[0]), "+v"(sw[1]));
+        // With one column block the last MFMA of the previous step wrote scur itself;
+        // it still ran before slot 0's MFMA could issue.
+        if constexpr (NQB == 2) {
+          asm volatile("s_nop 1" : "+v"(sw[0]), "+v"(sw[1]));
+        } else {
+          asm volatile("s_nop 1" : "+v"(sw[0]));
+        }
       } else if constexpr (s < NAS && a_begin(s) < 16) {
         asm volatile("" : "+v"(sw[0]));
       }
-      if constexpr (s < NAS && a_begin(s + 1) > 16) asm volatile("" : "+v"(sw[1]));
+      if constexpr (NQB == 2 && s < NAS && a_begin(s + 1) > 16) asm volatile("" : "+v"(sw[NQB - 1]));
       if constexpr (s >= 1) {
 #pragma unroll
         for (int e = a_begin(s - 1); e < a_begin(s); ++e) asm volatile("" : "+v"(tvw[e >> 4][e & 15]));
@@ -581,31 +609,32 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   uint64_t big_rows = 0;  // ballot of rows whose terms grew too large
   auto check_softmax = [&]() {
     if constexpr (kExp) {
-      const bool big = (sum[0][0] + sum[0][1] > kSumLimit) || (sum[1][0] + sum[1][1] > kSumLimit);
+      bool big = sum[0][0] + sum[0][1] > kSumLimit;
+      if constexpr (NQB == 2) big = big || (sum[1][0] + sum[1][1] > kSumLimit);
       big_rows = __builtin_amdgcn_ballot_w64(big);
     }
   };
   auto finish_softmax = [&]() {
     if constexpr (kExp) {
       if (big_rows != 0) {
-        float alpha[2];
+        float alpha[NQB];
         move_reference<kMasked>(scur, w.m, w.l, alpha, c, nv8);
-        w.alpha[0] = alpha[0];
-        w.alpha[1] = alpha[1];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) w.alpha[qb] = alpha[qb];
         w.rescale = kPV;  // before the first PV product acc is zero: nothing to rescale
         static_for<0, NE>(stage_a);
         static_for<0, NE>(stage_b);
         static_for<0, NE>(stage_c);
       }
-      w.l[0] += sum[0][0] + sum[0][1];
-      w.l[1] += sum[1][0] + sum[1][1];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) w.l[qb] += sum[qb][0] + sum[qb][1];
     }
   };
 
   // Reads issued before the first slot.
   static_for<0, NPAIR>([&](auto p_tag) {
     constexpr int p = decltype(p_tag)::value;
-    if constexpr (2 * (p - kVLead) < 0) load_v(p_tag);
+    if constexpr (NQB * (p - kVLead) < 0) load_v(p_tag);
   });
   if constexpr (kKStart == 0) static_for<0, 3>(load_k);
   if constexpr (kExp && NAS == 0) {  // too few slots to carry the softmax: do it before any MFMA
@@ -616,31 +645,31 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   }
 
   // PV slots whose d-block is 1 are followed by the row-sum MFMA of their P^T operand.
-  auto rowsum_after = [](int s) constexpr { return s < NPV && (s / 2) % DB == 1; };
+  auto rowsum_after = [](int s) constexpr { return s < NPV && (s / NQB) % DB == 1; };
   static_for<0, NS>([&](auto s_tag) {
     constexpr int s = decltype(s_tag)::value;
     if constexpr (s < NPV) {
-      constexpr int pr = s / 2, qb = s % 2;
+      constexpr int pr = s / NQB, qb = s % NQB;
       constexpr int h = pr / DB, db = pr % DB;
       mfma_o(w.acc[db][qb], vf[pr], pprev[qb][h]);
       // V pairs kVLead pairs ahead of their first slot.
       static_for<0, NPAIR>([&](auto p_tag) {
         constexpr int p = decltype(p_tag)::value;
-        if constexpr (2 * (p - kVLead) == s) load_v(p_tag);
+        if constexpr (NQB * (p - kVLead) == s) load_v(p_tag);
       });
     } else {
-      constexpr int ks = (s - NPV) / 2, qb = (s - NPV) % 2;
+      constexpr int ks = (s - NPV) / NQB, qb = (s - NPV) % NQB;
       if constexpr (ks == 0) {
         mfma_s0(snxt[qb], kf[ks], w.qf[qb][ks]);
       } else {
         mfma_s(snxt[qb], kf[ks], w.qf[qb][ks]);
       }
       // read ahead the next step's first V pairs
-      if constexpr (qb == 1 && ks < kVPre) prefetch_next(std::integral_constant<int, ks>{});
+      if constexpr (qb == NQB - 1 && ks < kVPre) prefetch_next(std::integral_constant<int, ks>{});
     }
-    // K operand reads: three k-steps ahead, starting kKStart slots in.
-    if constexpr (kQK && s >= kKStart && (s - kKStart) % 2 == 0) {
-      constexpr int n = (s - kKStart) / 2;  // n-th K read of this step, needed at slot NPV + 2n
+    // K operand reads, starting kKStart slots in.
+    if constexpr (kQK && s >= kKStart && (s - kKStart) % NQB == 0) {
+      constexpr int n = (s - kKStart) / NQB;  // n-th K read of this step, needed at slot NPV + NQB*n
       if constexpr (kKStart > 0) {
         load_k(std::integral_constant<int, n>{});
       } else {
@@ -660,7 +689,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (rowsum_after(s)) {
-      constexpr int qb = s % 2, h = (s / 2) / DB;
+      constexpr int qb = s % NQB, h = (s / NQB) / DB;
       mfma_rowsum(w.lbacc[qb], w.sel, pprev[qb][h]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -673,12 +702,18 @@ __device__ __forceinline__ void pipeline_step(Wave<D>& w, int j, int T, int N, c
   finish_softmax();
 }
 
-template <int D>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// NQB = 2: 256 query rows per workgroup, one wave per SIMD. NQB = 1: 128 rows
+// per workgroup; at d = 64 its registers allow two waves per SIMD and two
+// workgroups' K/V rings fit in LDS, so two workgroups share a CU. (At d = 128 the
+// 128 KB ring allows one workgroup per CU whatever the registers.)
+template <int D, int NQB>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(D == 64 ? 3 - NQB : 1, D == 64 ? 3 - NQB : 1)))
 fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
               __bf16* __restrict__ o, float* __restrict__ lse, int N, int tiles_per_head, int total_tiles,
               float c /* scale * log2(e) */, int order) {
   using C = Cfg<D>;
+  constexpr int kRowsPerWave = 32 * NQB;
+  constexpr int kBR = C::kWaves * kRowsPerWave;
   __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
   // The LDS base as a scalar: every LDS address below is a scalar offset plus at
   // most one per-lane term.
@@ -695,9 +730,9 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   const char* gv = (const char*)(v + head_off);
   const int T = (N + C::kBC - 1) / C::kBC;  // K/V tiles in LDS
   const int U = (N + 31) / 32;              // 32-key sub-tiles processed by the pipeline
-  const int q0 = qtile * C::kBR + wave * C::kRowsPerWave;
+  const int q0 = qtile * kBR + wave * kRowsPerWave;
 
-  Wave<D> w;
+  Wave<D, NQB> w;
 #pragma unroll
   for (int i = 0; i < C::kLoadsPerWave; ++i) {
     int row;
@@ -710,7 +745,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
 
   // Q^T operand fragments: lane holds query q0 + qb*32 + lane%32, d = ks*16 + g*8 .. +8.
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const int row = q0 + qb * 32 + (lane & 31);
     const bf16x8_t* src = (const bf16x8_t*)(q + head_off + (size_t)min(row, N - 1) * D + g * 8);
 #pragma unroll
@@ -722,7 +757,13 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   }
   // Wait states between the AGPR writes of Q^T and the first MFMA that reads them.
 #pragma unroll
-  for (int ks = 0; ks < C::kKS; ++ks) asm volatile("s_nop 1" : "+a"(w.qf[0][ks]), "+a"(w.qf[1][ks]));
+  for (int ks = 0; ks < C::kKS; ++ks) {
+    if constexpr (NQB == 2) {
+      asm volatile("s_nop 1" : "+a"(w.qf[0][ks]), "+a"(w.qf[1][ks]));
+    } else {
+      asm volatile("s_nop 1" : "+a"(w.qf[0][ks]));
+    }
+  }
   asm volatile("s_nop 7" ::: "memory");
   // Per-lane LDS byte offsets of the operand reads (sub-tile base added later; the
   // swizzle depends on row bits 0-3 only, so 16-row-aligned bases keep it).
@@ -748,10 +789,12 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
       asm volatile("" : "+v"(w.voff2[db][r]));
     }
   }
-  w.m[0] = w.m[1] = -__builtin_inff();
-  w.l[0] = w.l[1] = 0.0f;
-  w.lbacc[0] = f32x4_t{};
-  w.lbacc[1] = f32x4_t{};
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    w.m[qb] = -__builtin_inff();
+    w.l[qb] = 0.0f;
+    w.lbacc[qb] = f32x4_t{};
+  }
   {
     // Selector: lane l holds row l%16 of k-group l/16; 1 where rows 0-7 meet
     // k-groups 0, 2 and rows 8-15 meet k-groups 1, 3.
@@ -760,11 +803,12 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
     w.sel = __builtin_bit_cast(bf16x8_t, (u32x4_t){word, word, word, word});
   }
   w.rescale = false;
-  w.alpha[0] = w.alpha[1] = 1.0f;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) w.alpha[qb] = 1.0f;
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) {
-    w.acc[db][0] = f32x16_t{};
-    w.acc[db][1] = f32x16_t{};
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) w.acc[db][qb] = f32x16_t{};
   }
 
   wait_vmem();
@@ -782,28 +826,33 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   const int nvalid_last = N - (U - 1) * 32;  // 1..32 keys in the last sub-tile
   const bool ragged = nvalid_last < 32;
   const int nv8 = nvalid_last - 8 * g;
-  f32x16_t sa[2], sb[2];
-  bf16x8_t pa[2][2], pb[2][2];
+  f32x16_t sa[NQB], sb[NQB];
+  bf16x8_t pa[NQB][2], pb[NQB][2];
 
   // Scores of sub-tile 0.
   {
 #pragma unroll
     for (int ks = 0; ks < C::kKS; ++ks) {
       const bf16x8_t kfr = *(const LDS_AS bf16x8_t*)(uintptr_t)w.koff[ks];
-      if (ks == 0) {
-        mfma_s0(sa[0], kfr, w.qf[0][ks]);
-        mfma_s0(sa[1], kfr, w.qf[1][ks]);
-      } else {
-        mfma_s(sa[0], kfr, w.qf[0][ks]);
-        mfma_s(sa[1], kfr, w.qf[1][ks]);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        if (ks == 0) {
+          mfma_s0(sa[qb], kfr, w.qf[qb][ks]);
+        } else {
+          mfma_s(sa[qb], kfr, w.qf[qb][ks]);
+        }
       }
     }
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(sa[0]), "+v"(sa[1]));
+    if constexpr (NQB == 2) {
+      asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(sa[0]), "+v"(sa[1]));
+    } else {
+      asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(sa[0]));
+    }
   }
   // The reference max starts at sub-tile 0's row max (move_reference from m = -inf:
   // alpha = 0 and l stays 0), so the first softmax step takes the fast path.
   {
-    float alpha0[2];
+    float alpha0[NQB];
     if (U == 1 && ragged) move_reference<true>(sa, w.m, w.l, alpha0, c, nv8);
     else move_reference<false>(sa, w.m, w.l, alpha0, c, nv8);
   }
@@ -811,7 +860,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   // Step j: PV of j-1, softmax of j, scores of j+1. Two score buffers alternate,
   // so the softmax of j can spread over every MFMA slot of the step.
 #define FA_STEPP(JP, PV, EXP, QK, MASK, J, SC, SN, PP, PC) \
-  pipeline_step<D, PV, EXP, QK, MASK, JP>(w, J, T, N, gk, gv, lds, wave, lane, SC, SN, PP, PC, c, nv8)
+  pipeline_step<D, NQB, PV, EXP, QK, MASK, JP>(w, J, T, N, gk, gv, lds, wave, lane, SC, SN, PP, PC, c, nv8)
 #define FA_STEP(PV, EXP, QK, MASK, J, SC, SN, PP, PC) FA_STEPP(-1, PV, EXP, QK, MASK, J, SC, SN, PP, PC)
   if (U == 1) {
     if (ragged) FA_STEP(false, true, false, true, 0, sa, sb, pb, pa);
@@ -867,25 +916,29 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   // Epilogue: O = acc / lb (bf16, nearest-even), LSE = ln2 * (m + log2 l). O is
   // divided by the sum of the bf16-rounded terms that formed acc, so the weights
   // it applies to V sum to one exactly; LSE takes the sum of the unrounded terms.
-#pragma unroll
-  for (int db = 0; db < C::kDB; ++db) sync_acc(w.acc[db][0], w.acc[db][1]);
-  asm volatile("" : "+v"(w.lbacc[0]), "+v"(w.lbacc[1]));  // read after sync_acc's wait
+  sync_acc_all(w.acc);
+  // read after sync_acc's wait
+  if constexpr (NQB == 2) {
+    asm volatile("" : "+v"(w.lbacc[0]), "+v"(w.lbacc[1]));
+  } else {
+    asm volatile("" : "+v"(w.lbacc[0]));
+  }
   // The rounded-term sum of query q (this lane's q = lane%32) sits in lane q for
   // q < 16 and lane q + 16 otherwise (see mfma_rowsum).
   const int q32 = lane & 31;
   const int lb_src = (q32 < 16 ? q32 : q32 + 16) * 4;
   // O goes through LDS: each lane holds 8-byte pieces of 32 different rows, so
   // storing it directly would take 32 scattered stores per lane. Written into a
-  // row-major tile of this wave's 64 rows (row pitch padded by 16 bytes against
-  // bank conflicts) and read back by rows, it leaves as 16 fully coalesced 16-byte
-  // stores per lane. The K/V stages are idle by then: the barrier waits until every
+  // row-major tile of this wave's rows (row pitch padded by 16 bytes against
+  // bank conflicts) and read back by rows, it leaves as fully coalesced 16-byte
+  // stores (16 per lane at 64 rows per wave and d = 128). The K/V stages are idle by then: the barrier waits until every
   // wave has finished its last step (and, with the vmem wait above, every load).
   __syncthreads();
   constexpr int kOPitch = D * 2 + 16;
-  static_assert(C::kWaves * 64 * kOPitch <= C::kLdsBytes, "O staging tiles must fit in the K/V stages");
-  const unsigned otile = (unsigned)(uintptr_t)lds + (unsigned)(wave * 64 * kOPitch);
+  static_assert(C::kWaves * kRowsPerWave * kOPitch <= C::kLdsBytes, "O staging tiles must fit in the K/V stages");
+  const unsigned otile = (unsigned)(uintptr_t)lds + (unsigned)(wave * kRowsPerWave * kOPitch);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const float lsum = pair_sum(w.l[qb]);
     const float lbq = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(lb_src, __builtin_bit_cast(int, w.lbacc[qb][0])));
     const float inv = 1.0f / lbq;
@@ -906,7 +959,7 @@ fa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const 
   // Read back by rows: 16-byte chunk c = lane + 64*k is row c / kChunks, chunk c % kChunks.
   constexpr int kRowsPerPass = 64 / C::kChunks;
 #pragma unroll
-  for (int k = 0; k < C::kChunks; ++k) {
+  for (int k = 0; k < kRowsPerWave / kRowsPerPass; ++k) {
     const int r = k * kRowsPerPass + lane / C::kChunks, ch = lane % C::kChunks;
     const bf16x8_t x = *(const LDS_AS bf16x8_t*)(uintptr_t)(otile + (unsigned)(r * kOPitch + ch * 16));
     const int row = q0 + r;
@@ -935,18 +988,23 @@ int device_is_gfx950() {
 
 int launch_fused(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                  float scale, const Blocks& blk, void* stream, int order) {
-  (void)blk;
-  const int tiles = (N + 255) / 256;
+  // The compiled shapes: 4 waves, 64-key K/V tiles, 256 or 128 query rows.
+  if (blk.nwaves != 4 || blk.bc != 64 || (blk.br != 256 && blk.br != 128)) return FA_ERR_SHAPE;
+  const int tiles = (N + blk.br - 1) / blk.br;
   const long long total = (long long)B * H * tiles;
   const float c = scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
+#define FA_LAUNCH(D, NQB)                                                                                        \
+  hipLaunchKernelGGL((fa_fwd_kernel<D, NQB>), dim3((unsigned)total), dim3(256), 0, s, (const __bf16*)q,           \
+                     (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, tiles, (int)total, c, order)
   if (d == 128) {
-    hipLaunchKernelGGL(fa_fwd_kernel<128>, dim3((unsigned)total), dim3(256), 0, s, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, tiles, (int)total, c, order);
+    if (blk.br == 256) FA_LAUNCH(128, 2);
+    else FA_LAUNCH(128, 1);
   } else {
-    hipLaunchKernelGGL(fa_fwd_kernel<64>, dim3((unsigned)total), dim3(256), 0, s, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, tiles, (int)total, c, order);
+    if (blk.br == 256) FA_LAUNCH(64, 2);
+    else FA_LAUNCH(64, 1);
   }
+#undef FA_LAUNCH
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -6,12 +6,29 @@
 // "常见误区"). On gfx950 the limits are: 160 KB LDS per CU, 512 VGPR+AGPR per lane
 // at one wave per SIMD, and 32x32x16 bf16 MFMA tiles.
 //
-// Shape used for both head dimensions: 4 waves, each owning 64 query rows
-// (BR = 256), K/V tiles of 64 keys. Each wave reads every K/V tile from LDS, so
-// LDS bytes per MFMA flop fall as rows per wave rise; 64 rows keep the K and V
-// operand traffic (K by 128-bit reads, V by transposing 64-bit reads) within the
-// LDS read rate while the O accumulator (64 x d fp32) and Q (64 x d bf16) stay in
-// registers. Four K/V stages of 2*64*d*2 bytes use 128 KB at d = 128.
+// Two compiled shapes, both 4 waves with K/V tiles of 64 keys:
+//  * BR = 256: each wave owns 64 query rows. Each wave reads every K/V tile from
+//    LDS, so LDS bytes per MFMA flop fall as rows per wave rise; 64 rows keep the
+//    K and V operand traffic (K by 128-bit reads, V by transposing 64-bit reads)
+//    within the LDS read rate while the O accumulator (64 x d fp32) and Q (64 x d
+//    bf16) stay in registers. One workgroup per CU (its four K/V stages of
+//    2*64*d*2 bytes use 128 KB at d = 128; its registers allow one wave per SIMD).
+//  * BR = 128: 32 rows per wave, twice the LDS operand traffic per flop, but half
+//    the registers: two waves per SIMD, so at d = 64 (64 KB of stages) two
+//    workgroups share a CU and one's softmax runs under the other's MFMAs.
+// The selector estimates each shape's time as (rounds of resident workgroups) x
+// (time of one round) and keeps the faster; ties keep 256. Round times relative
+// to a round of 256-row workgroups, measured on one MI355X over 14 shapes:
+//  * d = 128, one resident workgroup per CU either way: a 128-row round takes
+//    0.59-0.60 of a 256-row round when both heights fill the chip. With twice the
+//    rounds, 128 wins only where the 256-row grid's last round is at most about
+//    half full (a grid of at most 128 tiles: measured 0.72-0.83 of the 256-row
+//    time), and 256 everywhere else (128 measured 1.16-1.19 times slower).
+//  * d = 64, two resident 128-row workgroups per CU: their round takes 0.93-1.0 of
+//    a 256-row round, and with twice the workgroups and twice the residency the
+//    round counts are equal, so 128 wins, by 25% when the 256-row grid leaves CUs
+//    idle.
+
 #include "fa_internal.h"
 
 #include <algorithm>
@@ -20,23 +37,35 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4, kRowsPerWave = 64, kKeysPerTile = 64, kStages = 4;
+constexpr int kWaves = 4, kKeysPerTile = 64, kStages = 4;
 constexpr int kLdsPerCu = 160 * 1024;
+constexpr int kCus = 256;  // MI355X; fixed so that a shape's results never depend on the device
 
 constexpr int lds_bytes(int d) { return kStages * 2 * kKeysPerTile * d * 2; }
 static_assert(lds_bytes(128) <= kLdsPerCu && lds_bytes(64) <= kLdsPerCu, "K/V ring must fit in LDS");
 
+// Workgroups of one shape resident per CU: LDS-bound (1 or 2), and 1 for BR = 256
+// (one wave per SIMD).
+constexpr int resident(int d, int br) { return br == 256 ? 1 : (2 * lds_bytes(d) <= kLdsPerCu ? 2 : 1); }
+
 }  // namespace
 
 Blocks select_blocks(int d, int N, int B, int H) {
-  (void)d;
-  (void)N;
-  (void)B;
-  (void)H;
   Blocks b;
   b.nwaves = kWaves;
-  b.br = kWaves * kRowsPerWave;
   b.bc = kKeysPerTile;
+  b.br = 256;
+  const int64_t bh = (int64_t)std::max(B, 0) * (int64_t)std::max(H, 0);
+  const int64_t n = std::max(N, 1);
+  // Time of a round of 128-row workgroups relative to a round of 256-row ones, in
+  // thousandths.
+  const int64_t rel128 = d == 64 ? 970 : 600;
+  auto cost = [&](int br, int64_t rel) {
+    const int64_t wgs = bh * ((n + br - 1) / br);
+    const int64_t slots = (int64_t)kCus * resident(d, br);
+    return (wgs + slots - 1) / slots * rel;
+  };
+  if (bh > 0 && cost(128, rel128) < cost(256, 1000)) b.br = 128;
   return b;
 }
 
@@ -51,7 +80,6 @@ Blocks select_blocks(int d, int N, int B, int H) {
 // multiples of 128 keys, a whole number of the kernel's key batches for both head
 // dimensions. Depends on the shape only, not on the device.
 namespace {
-constexpr int kCus = 256;
 int resident_per_cu(int Nq) { return Nq <= 1 ? 7 : Nq <= 2 ? 6 : Nq <= 4 ? 4 : Nq <= 8 ? 2 : 1; }
 }  // namespace
 

@@ -14,6 +14,7 @@
 
 namespace {
 int g_launches = 0;
+int g_last_br = 0;  // query-tile height of the last fused launch
 int g_device = 1;  // what device_is_gfx950 reports
 int g_failures = 0;
 
@@ -27,9 +28,10 @@ void expect(bool ok, const char* what, int line) {
 }  // namespace
 
 namespace fa {
-int launch_fused(const void*, const void*, const void*, void*, float*, int, int, int, int, float, const Blocks&,
+int launch_fused(const void*, const void*, const void*, void*, float*, int, int, int, int, float, const Blocks& blk,
                  void*, int) {
   ++g_launches;
+  g_last_br = blk.br;
   return FA_OK;
 }
 int launch_unfused(const void*, const void*, const void*, void*, float*, int, int, int, int, float, void*, void*) {
@@ -126,6 +128,25 @@ int main() {
   EXPECT(fa_unfused_fwd(q, k, v, o, lse, B, H, N, d, sc, q, need, nullptr) == FA_ERR_WORKSPACE);
   EXPECT(g_launches == before + 1);
 
+  // Explicit query-tile height: 128 and 256 launch with that height; any other
+  // height, and the usual argument errors, return before a launch. fa_fwd launches
+  // the selector's height.
+  {
+    const int before_blk = g_launches;
+    EXPECT(fa_fwd_blocks(q, k, v, o, lse, B, H, N, d, sc, 128, nullptr) == FA_OK && g_last_br == 128);
+    EXPECT(fa_fwd_blocks(q, k, v, o, lse, B, H, N, d, sc, 256, nullptr) == FA_OK && g_last_br == 256);
+    EXPECT(fa_fwd_blocks(q, k, v, o, lse, B, H, N, d, sc, 64, nullptr) == FA_ERR_SHAPE);
+    EXPECT(fa_fwd_blocks(q, k, v, o, lse, B, H, N, d, sc, 0, nullptr) == FA_ERR_SHAPE);
+    EXPECT(fa_fwd_blocks(q, k, v, q, lse, B, H, N, d, sc, 128, nullptr) == FA_ERR_ALIAS);
+    EXPECT(fa_fwd_blocks(q, k, v, o, lse, B, H, N, 96, sc, 128, nullptr) == FA_ERR_HEADDIM);
+    EXPECT(fa_fwd_blocks(nullptr, nullptr, nullptr, nullptr, nullptr, 0, H, N, d, sc, 128, nullptr) == FA_OK);
+    EXPECT(g_launches == before_blk + 2);
+    int sbr = 0, sbc = 0, snw = 0;
+    EXPECT(fa_select_blocks(d, N, B, H, &sbr, &sbc, &snw) == FA_OK);
+    EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, sc, nullptr) == FA_OK && g_last_br == sbr);
+    EXPECT(g_launches == before_blk + 3);
+  }
+
   // Decode: q/o hold Nq = 4 rows, k/v the N = 100 keys of each head.
   {
     g_device = 1;
@@ -184,7 +205,11 @@ int main() {
   // Selector and strings.
   int br = 0, bc = 0, nw = 0;
   EXPECT(fa_select_blocks(128, 8192, 1, 32, &br, &bc, &nw) == FA_OK && br == 256 && bc == 64 && nw == 4);
-  EXPECT(fa_select_blocks(64, 1024, 4, 16, &br, &bc, &nw) == FA_OK && br == 256 && bc == 64 && nw == 4);
+  EXPECT(fa_select_blocks(64, 1024, 4, 16, &br, &bc, &nw) == FA_OK && br == 128 && bc == 64 && nw == 4);
+  EXPECT(fa_select_blocks(128, 8192, 1, 8, &br, &bc, &nw) == FA_OK && br == 256);   // 256 tiles: one full round
+  EXPECT(fa_select_blocks(128, 8192, 1, 4, &br, &bc, &nw) == FA_OK && br == 128);   // 128 tiles: half the CUs
+  EXPECT(fa_select_blocks(128, 30001, 1, 8, &br, &bc, &nw) == FA_OK && br == 256);
+  EXPECT(fa_select_blocks(128, 8192, -1, 8, &br, &bc, &nw) == FA_ERR_SHAPE);
   EXPECT(fa_select_blocks(80, 1024, 4, 16, &br, &bc, &nw) == FA_ERR_HEADDIM);
   EXPECT(fa_select_blocks(64, 1024, 4, 16, nullptr, &bc, &nw) == FA_ERR_NULL);
   for (int s = FA_ERR_DEVICE; s <= FA_OK; ++s) {

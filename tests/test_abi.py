@@ -55,12 +55,20 @@ def test_version_and_status_strings(fa):
 
 def test_select_blocks(fa):
     for d in (64, 128):
-        br, bc, nw = fa.fa_select_blocks(d, 8192)
-        assert br == 64 * nw and bc in (32, 64, 128) and nw >= 1
-        # LDS budget: three K/V stages fit the 160 KB of a CU
-        assert 3 * 2 * bc * d * 2 <= 160 * 1024
+        for B, H, N in ((1, 1, 1), (1, 1, 8192), (4, 16, 1024), (1, 32, 8192), (1, 8, 30001), (64, 64, 65536)):
+            br, bc, nw = fa.fa_select_blocks(d, N, B, H)
+            assert br in (128, 256) and bc == 64 and nw == 4, (d, B, H, N)
+            assert br == fa.fa_select_blocks(d, N, B, H)[0]  # a function of the shape
+        # LDS budget: four K/V stages fit the 160 KB of a CU
+        assert 4 * 2 * bc * d * 2 <= 160 * 1024
+    # The benchmark shape fills the chip four times over with 256-row tiles: keep them.
+    assert fa.fa_select_blocks(128, 8192, 1, 32)[0] == 256
+    # One head of 8192 rows makes 32 tiles of 256 rows for 256 CUs: take 128 rows.
+    assert fa.fa_select_blocks(128, 8192, 1, 1)[0] == 128
     with pytest.raises(ValueError):
         fa.fa_select_blocks(96, 128)
+    with pytest.raises(ValueError):
+        fa.fa_select_blocks(128, -1)
 
 
 def test_workspace_bytes(fa):
