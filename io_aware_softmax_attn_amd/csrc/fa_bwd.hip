@@ -165,6 +165,55 @@ __device__ __forceinline__ int remap_xcd(int w, int total) {
   return xcd < rem ? xcd * (base + 1) + idx : rem * (base + 1) + (xcd - rem) * base + idx;
 }
 
+// Buffer resource over rows [row0, row0 + rows) of an array of `row_bytes`-wide rows
+// that has N rows: only the part inside N is mapped, so loads past it return zeros
+// without touching memory (the ragged last tile, and tiles past the end, need no
+// clamping). Word 3 selects raw 32-bit data (no swizzle, no index stride).
+constexpr unsigned kRawBufferWord3 = 0x00020000u;
+__device__ __forceinline__ u32x4_t rows_rsrc(const void* base, int row0, int rows, int N, int row_bytes) {
+  const int valid = min(max(N - row0, 0), rows);
+  const uint64_t a = (uint64_t)(uintptr_t)base + (uint64_t)(int64_t)row0 * (uint64_t)row_bytes;
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane((unsigned)(valid * row_bytes));
+  r[3] = kRawBufferWord3;
+  return r;
+}
+
+// Direct global->LDS loads (buffer_load ... lds): lane l's 16 (or 4) bytes at byte
+// offset voff of the resource land at LDS address lds_addr + 16*l (or 4*l). Issued
+// through asm so that the compiler does not put a vmcnt(0) wait in front of every
+// LDS read (it cannot tell that the destination stage is not the one being read);
+// the kernel waits for these loads itself (tile_barrier). M0 carries the LDS
+// address, with one wait state between its write and the load. The compiler warns
+// that M0 is reserved and its clobber not honoured: no other code in these kernels
+// uses M0, and each of these asm blocks sets it before its load.
+__device__ __forceinline__ void dma16(u32x4_t rsrc, unsigned voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(u32x4_t rsrc, unsigned voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Wait until at most kOutstanding of this wave's vector-memory loads are in flight
+// (they complete in issue order), then the workgroup barrier: after it every wave's
+// share of the tiles older than those is in LDS. The memory clobbers keep the
+// compiler from moving LDS accesses across it.
+template <int kOutstanding>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(kOutstanding >= 0 && kOutstanding <= 63, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOutstanding) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
@@ -300,8 +349,17 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
                                                        __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N,
                                                        int tiles_per_head, int total_tiles, float c, float scale) {
   constexpr int KS = D / 16, DB = D / 32, kTile = 32 * D * 2;
-  constexpr int kStage = 2 * kTile + 2 * 32 * 4;  // Q tile, dO tile, LSE2[32], D[32]
-  __shared__ __attribute__((aligned(1024))) char smem[3 * kStage];
+  // Ring of Q/dO tiles of 32 rows: each stage holds the Q tile, the dO tile and a
+  // 1 KB vector area (LSE2 of the tile's rows at +0, D at +256; +512 and +768 take
+  // the zero fills of the vector loads that waves 2 and 3 issue so that every wave
+  // issues the same number of loads per tile).
+  constexpr int kStages = 4, kVec = 1024;
+  constexpr int kStage = 2 * kTile + kVec;
+  constexpr int kChunks = D / 8;
+  constexpr int kLoads = kTile / 1024 / 4;  // 16-byte loads per wave per Q (or dO) tile
+  constexpr int kPerTile = 2 * kLoads + 1;  // this wave's loads per tile, vector load included
+  static_assert(kLoads >= 1 && kTile % 4096 == 0, "tile loads must split evenly over the 4 waves");
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
   const unsigned lds = (unsigned)(uintptr_t)(LDS_AS char*)smem;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
   const int logical = remap_xcd(blockIdx.x, total_tiles);
@@ -332,21 +390,36 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
   }
 
   const int T = (N + 31) / 32;
-  TileCopy<D, 32> cq, cdo;
-  // Row vectors of the tile: thread i < 32 copies LSE2 of row i, thread 32 + i its D.
-  float vec = 0.0f;
-  auto load_tile = [&](int row0) {
-    cq.load(q + head, row0, N);
-    cdo.load(dO + head, row0, N);
-    const int i = threadIdx.x & 31, r = row0 + i;
-    if (threadIdx.x < 32) vec = r < N ? lse2[rowvec + r] : __builtin_inff();  // padded rows: P = 0
-    else if (threadIdx.x < 64) vec = r < N ? dvec[rowvec + r] : 0.0f;
+  // Loads: tile u's Q and dO rows go straight from global memory into a stage
+  // (buffer_load ... lds, 16 bytes per lane, in the swizzled layout that read_row and
+  // read_tr expect), and so do its 32 LSE2 and D values (4 bytes per lane). Lane l's
+  // 16 bytes of load i form slot p = (wave * kLoads + i) * 64 + l of the tile: row
+  // p / kChunks, physical chunk p % kChunks, i.e. logical chunk (p % kChunks) ^ swz.
+  unsigned gofs[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int p = (wave * kLoads + i) * 64 + lane, row = p / kChunks;
+    gofs[i] = (unsigned)(row * D * 2 + (((p % kChunks) ^ swz<D>(row)) << 4));
+  }
+  const char* qh = (const char*)(q + head);
+  const char* dh = (const char*)(dO + head);
+  // part 0: Q rows, 1: dO rows, 2: the vector (wave 0 LSE2, wave 1 D, waves 2-3 an
+  // empty resource). Rows past N, and tiles past the end, read as zeros: their Q and
+  // dO rows are zero, so S = 0 and P = exp2(0 - 0) = 1 there, while dP = D = 0 gives
+  // dS = 0 and the zero dO row adds nothing to dV.
+  auto issue = [&](int part, int u, unsigned st) {
+    if (part < 2) {
+      const u32x4_t r = rows_rsrc(part == 0 ? qh : dh, u * 32, 32, N, D * 2);
+      const unsigned dst = __builtin_amdgcn_readfirstlane(st + (unsigned)(part * kTile + wave * kLoads * 1024));
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) dma16(r, gofs[i], dst + i * 1024);
+    } else {
+      const float* src = (wave == 0 ? lse2 : dvec) + rowvec;
+      const u32x4_t r = rows_rsrc(src, u * 32, 32, wave < 2 ? N : 0, 4);
+      dma4(r, (unsigned)lane * 4u, __builtin_amdgcn_readfirstlane(st + (unsigned)(2 * kTile + wave * 256)));
+    }
   };
-  auto store_tile = [&](unsigned st) {
-    cq.store(st);
-    cdo.store(st + kTile);
-    if (threadIdx.x < 64) *(LDS_AS float*)(uintptr_t)(st + 2 * kTile + 4 * threadIdx.x) = vec;
-  };
+  auto stage_of = [&](int u) { return lds + (unsigned)((u & (kStages - 1)) * kStage); };
   // S and dP of the tile at st: KS products each, in ks order. The row operands
   // are read one step ahead: loads do not move across the asm MFMAs, so reading
   // them right before their product would expose the LDS latency.
@@ -359,27 +432,34 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
       mfma_sv(dp, ad, vf[ks]);
     }
   };
-  // Three stages: while tile t's softmax runs on the VALU, the matrix cores compute
-  // S and dP of tile t+1, and tile t+2 is in flight from memory. The softmax is cut
-  // into four parts placed between the product pairs, each pinned to its place
-  // (inputs at its start, outputs at its end) so the VALU work interleaves with the
-  // MFMAs instead of running before them. Tiles past the end are zero rows with
-  // LSE2 = +inf (P = 0), so every step runs the same code.
-  unsigned cur = lds, nxt = lds + kStage, fut = lds + 2 * kStage;
-  load_tile(0);
-  store_tile(cur);
-  load_tile(32);
-  store_tile(nxt);
-  __syncthreads();
-  f32x16_t s, dp;
+  // Pipeline: while tile t's softmax runs on the VALU, the matrix cores compute S
+  // and dP of tile t+1, and tiles t+2 and t+3 are in flight from memory: tile t+3's
+  // loads go out during step t into the stage that tile t-1 used (its last reads
+  // were consumed by step t-1's products, before the barrier ending that step), and
+  // the barrier ending step t+1 waits for them. The softmax is cut into four parts
+  // placed between the product pairs, each pinned to its place (inputs at its start,
+  // outputs at its end) so the VALU work interleaves with the MFMAs instead of
+  // running before them. Tiles past the end are zero rows, so every step runs the
+  // same code.
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    sdp_step(ks, read_row<D>(cur, ks, lane), read_row<D>(cur + kTile, ks, lane), s, dp);
+  for (int u = 0; u < kStages - 1; ++u) {
+    issue(0, u, stage_of(u));
+    issue(1, u, stage_of(u));
+    issue(2, u, stage_of(u));
+  }
+  tile_barrier<kPerTile>();  // tiles 0 and 1 landed; tile 2 may stay in flight
+  f32x16_t s, dp;
+  {
+    const unsigned cur = stage_of(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sdp_step(ks, read_row<D>(cur, ks, lane), read_row<D>(cur + kTile, ks, lane), s, dp);
+  }
   sync_sv(s, dp);
   for (int t = 0; t < T; ++t) {
-    load_tile((t + 2) * 32);
+    const unsigned cur = stage_of(t), nxt = stage_of(t + 1), fut = stage_of(t + kStages - 1);
     const LDS_AS float* l2v = (const LDS_AS float*)(uintptr_t)(cur + 2 * kTile);
-    const LDS_AS float* dvv = l2v + 32;
+    const LDS_AS float* dvv = l2v + 64;
     float p[16], ds[16];
     f32x16_t s2, dp2;
     bf16x8_t rq[KS], rd[KS];  // row operands of tile t+1; only a window is live at once
@@ -391,6 +471,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
     }
 #pragma unroll
     for (int part = 0; part < 4; ++part) {
+      if (part < 3) issue(part, t + kStages - 1, fut);
       if (part + 1 < 4) {
 #pragma unroll
         for (int ks = (part + 1) * kPer; ks < (part + 2) * kPer; ++ks) {
@@ -441,18 +522,17 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
       mfma_acc(adk[db], tr[db][2], s0);
       mfma_acc(adk[db], tr[db][3], s1);
     }
-    store_tile(fut);
-    __syncthreads();
+    // Tile t+2 (read from step t+1 on) has landed; tile t+3 may stay in flight.
+    tile_barrier<kPerTile>();
     // The products of S2 and dP2 were issued before the 4*DB accumulator products;
     // the pin still covers the wait states before the VALU reads them.
     sync_sv(s2, dp2);
     s = s2;
     dp = dp2;
-    const unsigned done = cur;
-    cur = nxt;
-    nxt = fut;
-    fut = done;
   }
+  // Loads issued past the last tile (zero fills) must land before the workgroup's
+  // LDS can be handed to another workgroup.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int db = 0; db < DB; ++db) sync_acc(adk[db], adv[db]);
   if (krow < N) {
