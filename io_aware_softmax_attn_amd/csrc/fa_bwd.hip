@@ -130,33 +130,6 @@ __device__ __forceinline__ bf16x8_t read_row(unsigned tile, int ks, int lane) {
   return *(const LDS_AS bf16x8_t*)(uintptr_t)(tile + chunk_offset<D>(pi_row(lane & 31), 2 * ks + (lane >> 5)));
 }
 
-// Cooperative copy of `rows` consecutive rows (from row0 of a [N, D] head; rows past
-// N read as zero) into an LDS tile, one 16-byte chunk per thread per step. The
-// values are returned in registers first (load) and written later (store), so the
-// global loads of the next tile overlap the current tile's products.
-template <int D, int kRows>
-struct TileCopy {
-  static constexpr int kChunks = D / 8;
-  static constexpr int kPerThread = kRows * kChunks / 256;
-  static_assert(kRows * kChunks % 256 == 0, "tile must split evenly over 256 threads");
-  u32x4_t r[kPerThread];
-  __device__ __forceinline__ void load(const __bf16* head, int row0, int N) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int idx = threadIdx.x + 256 * i, row = idx / kChunks, ch = idx % kChunks;
-      r[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (row0 + row < N) r[i] = *(const u32x4_t*)(head + (size_t)(row0 + row) * D + ch * 8);
-    }
-  }
-  __device__ __forceinline__ void store(unsigned tile) const {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int idx = threadIdx.x + 256 * i, row = idx / kChunks, ch = idx % kChunks;
-      *(LDS_AS u32x4_t*)(uintptr_t)(tile + chunk_offset<D>(row, ch)) = r[i];
-    }
-  }
-};
-
 // Workgroup id -> logical tile id such that each XCD (ids w with w % 8 == x) gets
 // a contiguous range: a head's tiles share one L2.
 __device__ __forceinline__ int remap_xcd(int w, int total) {
@@ -259,7 +232,13 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
                                                      __bf16* __restrict__ dq, int N, int tiles_per_head,
                                                      int total_tiles, float c, float scale) {
   constexpr int KS = D / 16, DB = D / 32, kTile = 32 * D * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTile];  // 2 stages x (K, V)
+  // Ring of 32-key K/V tiles: each stage holds the K tile, then the V tile.
+  constexpr int kStages = 4, kStage = 2 * kTile;
+  constexpr int kChunks = D / 8;
+  constexpr int kLoads = kTile / 1024 / 4;  // 16-byte loads per wave per K (or V) tile
+  constexpr int kPerTile = 2 * kLoads;      // this wave's loads per K/V tile
+  static_assert(kLoads >= 1 && kTile % 4096 == 0, "tile loads must split evenly over the 4 waves");
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
   const unsigned lds = (unsigned)(uintptr_t)(LDS_AS char*)smem;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
   const int logical = remap_xcd(blockIdx.x, total_tiles);
@@ -284,18 +263,38 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
 
   const int T = (N + 31) / 32;
-  TileCopy<D, 32> ck, cv;
-  ck.load(k + head, 0, N);
-  cv.load(v + head, 0, N);
-  ck.store(lds);
-  cv.store(lds + kTile);
-  __syncthreads();
+  // K and V rows go straight from global memory into a stage (buffer_load ... lds,
+  // 16 bytes per lane, in the swizzled layout that read_row and read_tr expect):
+  // lane l's load i is slot p = (wave * kLoads + i) * 64 + l of the tile, row
+  // p / kChunks, logical chunk (p % kChunks) ^ swz. Keys past N read as zeros, and
+  // their P is set to 0 below.
+  unsigned gofs[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int p = (wave * kLoads + i) * 64 + lane, row = p / kChunks;
+    gofs[i] = (unsigned)(row * D * 2 + (((p % kChunks) ^ swz<D>(row)) << 4));
+  }
+  const char* kh = (const char*)(k + head);
+  const char* vh = (const char*)(v + head);
+  auto issue = [&](int u, unsigned st) {
+    const u32x4_t rk = rows_rsrc(kh, u * 32, 32, N, D * 2);
+    const u32x4_t rv = rows_rsrc(vh, u * 32, 32, N, D * 2);
+    const unsigned dst = __builtin_amdgcn_readfirstlane(st + (unsigned)(wave * kLoads * 1024));
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) dma16(rk, gofs[i], dst + i * 1024);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) dma16(rv, gofs[i], dst + kTile + i * 1024);
+  };
+  auto stage_of = [&](int u) { return lds + (unsigned)((u & (kStages - 1)) * kStage); };
+  // Tile t+3's loads go out during step t into the stage tile t-1 used (its reads
+  // were consumed by step t-1's products, before the barrier ending that step); the
+  // barrier ending step t+2 waits for them, so each tile has three steps to land.
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u) issue(u, stage_of(u));
+  tile_barrier<2 * kPerTile>();  // tile 0 landed; tiles 1 and 2 may stay in flight
   for (int t = 0; t < T; ++t) {
-    const unsigned kt = lds + (t & 1) * 2 * kTile, vt = kt + kTile;
-    if (t + 1 < T) {
-      ck.load(k + head, (t + 1) * 32, N);
-      cv.load(v + head, (t + 1) * 32, N);
-    }
+    const unsigned kt = stage_of(t), vt = kt + kTile;
+    issue(t + kStages - 1, stage_of(t + kStages - 1));
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -315,13 +314,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
       acc[db] = mfma(read_tr<D>(kt, 0, db * 32, lane), b0, acc[db]);
       acc[db] = mfma(read_tr<D>(kt, 16, db * 32, lane), b1, acc[db]);
     }
-    if (t + 1 < T) {
-      const unsigned nt = lds + ((t + 1) & 1) * 2 * kTile;
-      ck.store(nt);
-      cv.store(nt + kTile);
-    }
-    __syncthreads();
+    // Tile t+1 has landed; tiles t+2 and t+3 may stay in flight.
+    tile_barrier<2 * kPerTile>();
   }
+  // Loads issued past the last tile (zero fills) must land before the workgroup's
+  // LDS can be handed to another workgroup.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // Lane holds dQ^T rows (columns of dQ) db*32 + 8*(i/4) + 4g + i%4 of query qrow.
   if (qrow < N) {
     __bf16* out = dq + head + (size_t)qrow * D;
