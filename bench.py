@@ -726,6 +726,9 @@ def main():
             "kernel_ms_min": round(min(per_launch_ms), 4),
             "flops_per_launch": w.flops,
             "min_hbm_bytes_per_launch": w.min_hbm_bytes,
+            # HBM rate of the counted bytes over the average launch, against the 8 TB/s roofline
+            "hbm_gb_per_s": None if traffic is None else round(traffic / (avg_ms * 1e-3) / 1e9, 1),
+            "hbm_frac_of_peak": None if traffic is None else round(traffic / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
     }
     if not args.launches_only and not args.no_cpu_baseline:
