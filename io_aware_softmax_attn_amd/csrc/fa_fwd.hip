@@ -19,7 +19,9 @@
 //    when K rows are fed to the MFMA) so that the accumulator layout of S^T
 //    matches the operand layout that ds_read_b64_tr_b16 produces for V^T. The
 //    contraction over keys does not depend on key order.
-//  * 4 waves x 64 query rows per workgroup (BR = 256), 64-key K/V tiles, four
+//  * 4 waves x 64 query rows per workgroup (BR = 256), or x 32 rows (BR = 128,
+//    for grids that 256-row tiles would leave partly idle, and for d = 64, where
+//    two such workgroups share a CU); 64-key K/V tiles, four
 //    LDS stages filled by direct global->LDS 16-byte loads (buffer_load_dwordx4
 //    ... lds, through per-tile buffer resources that read rows past N as zero)
 //    with a XOR swizzle of 16-byte chunks against LDS bank conflicts.
