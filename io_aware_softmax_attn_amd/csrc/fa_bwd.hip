@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/fa.h"
 #include "fa_internal.h"
@@ -417,10 +418,42 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
       dma4(r, (unsigned)lane * 4u, __builtin_amdgcn_readfirstlane(st + (unsigned)(2 * kTile + wave * 256)));
     }
   };
-  auto stage_of = [&](int u) { return lds + (unsigned)((u & (kStages - 1)) * kStage); };
-  // S and dP of the tile at st: KS products each, in ks order. The row operands
-  // are read one step ahead: loads do not move across the asm MFMAs, so reading
-  // them right before their product would expose the LDS latency.
+  // Per-lane LDS addresses of the operand reads for a stage at offset 0: the row
+  // reads of k-step ks (as read_row) and the two halves of the transposing reads of
+  // column block db (as read_tr with r0 = 0; r0 = 16 is 16 rows further, the swizzle
+  // depending on row bits 0-3 only). The loop below is unrolled over the four stages
+  // of the ring, so every stage offset is a constant and rides in the ds_read
+  // immediate (at most 3 * kStage + kTile + 16 rows < 64 KiB): no address
+  // arithmetic per read. The empty asm keeps the compiler from recomputing them.
+  unsigned rofs[KS], tofs[DB][2];
+  {
+    const int rr = pi_row(lane & 31), trow = 8 * g + ((lane & 15) >> 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      rofs[ks] = lds + (unsigned)chunk_offset<D>(rr, 2 * ks + g);
+      asm volatile("" : "+v"(rofs[ks]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      tofs[db][0] = lds + (unsigned)(chunk_offset<D>(trow, col >> 3) + 2 * (col & 7));
+      tofs[db][1] = lds + (unsigned)(chunk_offset<D>(trow + 4, col >> 3) + 2 * (col & 7));
+      asm volatile("" : "+v"(tofs[db][0]), "+v"(tofs[db][1]));
+    }
+  }
+  static_assert((kStages - 1) * kStage + kTile + 16 * 2 * D < 65536, "stage offsets must fit the ds_read immediate");
+  auto rd_row = [&](unsigned off, int ks) -> bf16x8_t {
+    return *(const LDS_AS bf16x8_t*)(uintptr_t)(rofs[ks] + off);
+  };
+  auto rd_tr = [&](unsigned off, int db) -> bf16x8_t {
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(tofs[db][0] + off));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(tofs[db][1] + off));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4,
+                                   5, 6, 7);
+  };
+  // S and dP of a tile: KS products each, in ks order. The row operands are read one
+  // window ahead: loads do not move across the asm MFMAs, so reading them right
+  // before their product would expose the LDS latency.
   auto sdp_step = [&](int ks, const bf16x8_t& aq, const bf16x8_t& ad, f32x16_t& s, f32x16_t& dp) {
     if (ks == 0) {
       mfma_sv0(s, aq, kf[ks]);
@@ -438,43 +471,30 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
   // placed between the product pairs, each pinned to its place (inputs at its start,
   // outputs at its end) so the VALU work interleaves with the MFMAs instead of
   // running before them. Tiles past the end are zero rows, so every step runs the
-  // same code.
-#pragma unroll
-  for (int u = 0; u < kStages - 1; ++u) {
-    issue(0, u, stage_of(u));
-    issue(1, u, stage_of(u));
-    issue(2, u, stage_of(u));
-  }
-  tile_barrier<kPerTile>();  // tiles 0 and 1 landed; tile 2 may stay in flight
-  f32x16_t s, dp;
-  {
-    const unsigned cur = stage_of(0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sdp_step(ks, read_row<D>(cur, ks, lane), read_row<D>(cur + kTile, ks, lane), s, dp);
-  }
-  sync_sv(s, dp);
-  for (int t = 0; t < T; ++t) {
-    const unsigned cur = stage_of(t), nxt = stage_of(t + 1), fut = stage_of(t + kStages - 1);
-    const LDS_AS float* l2v = (const LDS_AS float*)(uintptr_t)(cur + 2 * kTile);
+  // same code. Step t uses stage t % 4 (J below); S and dP alternate between two
+  // register sets, so no copy is needed between steps.
+  constexpr int kPer = KS / 4;
+  auto step = [&](auto j_tag, int t, f32x16_t& s, f32x16_t& dp, f32x16_t& s2, f32x16_t& dp2) {
+    constexpr int J = decltype(j_tag)::value;
+    constexpr unsigned CUR = J * kStage, NXT = ((J + 1) % kStages) * kStage;
+    constexpr unsigned FUT = ((J + kStages - 1) % kStages) * kStage;
+    const LDS_AS float* l2v = (const LDS_AS float*)(uintptr_t)(lds + CUR + 2 * kTile);
     const LDS_AS float* dvv = l2v + 64;
     float p[16], ds[16];
-    f32x16_t s2, dp2;
     bf16x8_t rq[KS], rd[KS];  // row operands of tile t+1; only a window is live at once
-    constexpr int kPer = KS / 4;
 #pragma unroll
     for (int ks = 0; ks < kPer; ++ks) {
-      rq[ks] = read_row<D>(nxt, ks, lane);
-      rd[ks] = read_row<D>(nxt + kTile, ks, lane);
+      rq[ks] = rd_row(NXT, ks);
+      rd[ks] = rd_row(NXT + kTile, ks);
     }
 #pragma unroll
     for (int part = 0; part < 4; ++part) {
-      if (part < 3) issue(part, t + kStages - 1, fut);
+      if (part < 3) issue(part, t + kStages - 1, lds + FUT);
       if (part + 1 < 4) {
 #pragma unroll
         for (int ks = (part + 1) * kPer; ks < (part + 2) * kPer; ++ks) {
-          rq[ks] = read_row<D>(nxt, ks, lane);
-          rd[ks] = read_row<D>(nxt + kTile, ks, lane);
+          rq[ks] = rd_row(NXT, ks);
+          rd[ks] = rd_row(NXT + kTile, ks);
         }
       }
 #pragma unroll
@@ -500,13 +520,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
       asm volatile("" : "+v"(p[4 * part]), "+v"(p[4 * part + 1]), "+v"(p[4 * part + 2]), "+v"(p[4 * part + 3]),
                    "+v"(ds[4 * part]), "+v"(ds[4 * part + 1]), "+v"(ds[4 * part + 2]), "+v"(ds[4 * part + 3]));
     }
-    // Transposed operands of the accumulator products, read one column block ahead.
+    // Transposed operands of the accumulator products (dO^T for dV, Q^T for dK, rows
+    // 0-15 and 16-31 of the tile), read one column block ahead.
     bf16x8_t tr[DB][4];
     auto read_block = [&](int db) {
-      tr[db][0] = read_tr<D>(cur + kTile, 0, db * 32, lane);
-      tr[db][1] = read_tr<D>(cur + kTile, 16, db * 32, lane);
-      tr[db][2] = read_tr<D>(cur, 0, db * 32, lane);
-      tr[db][3] = read_tr<D>(cur, 16, db * 32, lane);
+      tr[db][0] = rd_tr(CUR + kTile, db);
+      tr[db][1] = rd_tr(CUR + kTile + 16 * 2 * D, db);
+      tr[db][2] = rd_tr(CUR, db);
+      tr[db][3] = rd_tr(CUR + 16 * 2 * D, db);
     };
     read_block(0);
     bf16x8_t p0 = pack8(p), p1 = pack8(p + 8), s0 = pack8(ds), s1 = pack8(ds + 8);
@@ -525,9 +546,34 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
     // The products of S2 and dP2 were issued before the 4*DB accumulator products;
     // the pin still covers the wait states before the VALU reads them.
     sync_sv(s2, dp2);
-    s = s2;
-    dp = dp2;
+  };
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u) {
+    const unsigned st = lds + (unsigned)(u * kStage);
+    issue(0, u, st);
+    issue(1, u, st);
+    issue(2, u, st);
   }
+  tile_barrier<kPerTile>();  // tiles 0 and 1 landed; tile 2 may stay in flight
+  f32x16_t sA, dpA, sB, dpB;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) sdp_step(ks, rd_row(0, ks), rd_row(kTile, ks), sA, dpA);
+  sync_sv(sA, dpA);
+  static_assert(kStages == 4, "the unrolled loop below covers a ring of four stages");
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  int t = 0;
+  for (; t + kStages <= T; t += kStages) {
+    step(I0{}, t, sA, dpA, sB, dpB);
+    step(I1{}, t + 1, sB, dpB, sA, dpA);
+    step(I2{}, t + 2, sA, dpA, sB, dpB);
+    step(I3{}, t + 3, sB, dpB, sA, dpA);
+  }
+  if (t < T) step(I0{}, t, sA, dpA, sB, dpB);
+  if (t + 1 < T) step(I1{}, t + 1, sB, dpB, sA, dpA);
+  if (t + 2 < T) step(I2{}, t + 2, sA, dpA, sB, dpB);
   // Loads issued past the last tile (zero fills) must land before the workgroup's
   // LDS can be handed to another workgroup.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
