@@ -286,21 +286,48 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) dma16(rv, gofs[i], dst + kTile + i * 1024);
   };
-  auto stage_of = [&](int u) { return lds + (unsigned)((u & (kStages - 1)) * kStage); };
+  // Per-lane LDS addresses of the operand reads for a stage at offset 0 (as in the
+  // dK/dV kernel): the loop is unrolled over the four ring stages, so each stage
+  // offset rides in the ds_read immediate.
+  unsigned rofs[KS], tofs[DB][2];
+  {
+    const int rr = pi_row(lane & 31), trow = 8 * g + ((lane & 15) >> 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      rofs[ks] = lds + (unsigned)chunk_offset<D>(rr, 2 * ks + g);
+      asm volatile("" : "+v"(rofs[ks]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      tofs[db][0] = lds + (unsigned)(chunk_offset<D>(trow, col >> 3) + 2 * (col & 7));
+      tofs[db][1] = lds + (unsigned)(chunk_offset<D>(trow + 4, col >> 3) + 2 * (col & 7));
+      asm volatile("" : "+v"(tofs[db][0]), "+v"(tofs[db][1]));
+    }
+  }
+  static_assert((kStages - 1) * kStage + kTile + 16 * 2 * D < 65536, "stage offsets must fit the ds_read immediate");
+  auto rd_row = [&](unsigned off, int ks) -> bf16x8_t {
+    return *(const LDS_AS bf16x8_t*)(uintptr_t)(rofs[ks] + off);
+  };
+  auto rd_tr = [&](unsigned off, int db) -> bf16x8_t {
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(tofs[db][0] + off));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(tofs[db][1] + off));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4,
+                                   5, 6, 7);
+  };
   // Tile t+3's loads go out during step t into the stage tile t-1 used (its reads
   // were consumed by step t-1's products, before the barrier ending that step); the
   // barrier ending step t+2 waits for them, so each tile has three steps to land.
-#pragma unroll
-  for (int u = 0; u < kStages - 1; ++u) issue(u, stage_of(u));
-  tile_barrier<2 * kPerTile>();  // tile 0 landed; tiles 1 and 2 may stay in flight
-  for (int t = 0; t < T; ++t) {
-    const unsigned kt = stage_of(t), vt = kt + kTile;
-    issue(t + kStages - 1, stage_of(t + kStages - 1));
+  // Step t uses stage t % 4 (J below).
+  auto step = [&](auto j_tag, int t) {
+    constexpr int J = decltype(j_tag)::value;
+    constexpr unsigned KT = J * kStage, VT = KT + kTile;
+    issue(t + kStages - 1, lds + (unsigned)(((J + kStages - 1) % kStages) * kStage));
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = mfma(read_row<D>(kt, ks, lane), qf[ks], s);
-      dp = mfma(read_row<D>(vt, ks, lane), df[ks], dp);
+      s = mfma(rd_row(KT, ks), qf[ks], s);
+      dp = mfma(rd_row(VT, ks), df[ks], dp);
     }
     float ds[16];
 #pragma unroll
@@ -312,12 +339,30 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
     const bf16x8_t b0 = pack8(ds), b1 = pack8(ds + 8);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      acc[db] = mfma(read_tr<D>(kt, 0, db * 32, lane), b0, acc[db]);
-      acc[db] = mfma(read_tr<D>(kt, 16, db * 32, lane), b1, acc[db]);
+      acc[db] = mfma(rd_tr(KT, db), b0, acc[db]);
+      acc[db] = mfma(rd_tr(KT + 16 * 2 * D, db), b1, acc[db]);
     }
     // Tile t+1 has landed; tiles t+2 and t+3 may stay in flight.
     tile_barrier<2 * kPerTile>();
+  };
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u) issue(u, lds + (unsigned)(u * kStage));
+  tile_barrier<2 * kPerTile>();  // tile 0 landed; tiles 1 and 2 may stay in flight
+  static_assert(kStages == 4, "the unrolled loop below covers a ring of four stages");
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  int t = 0;
+  for (; t + kStages <= T; t += kStages) {
+    step(I0{}, t);
+    step(I1{}, t + 1);
+    step(I2{}, t + 2);
+    step(I3{}, t + 3);
   }
+  if (t < T) step(I0{}, t);
+  if (t + 1 < T) step(I1{}, t + 1);
+  if (t + 2 < T) step(I2{}, t + 2);
   // Loads issued past the last tile (zero fills) must land before the workgroup's
   // LDS can be handed to another workgroup.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
