@@ -318,9 +318,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
   // Tile t+3's loads go out during step t into the stage tile t-1 used (its reads
   // were consumed by step t-1's products, before the barrier ending that step); the
   // barrier ending step t+2 waits for them, so each tile has three steps to land.
-  // Step t uses stage t % 4 (J below).
-  auto step = [&](auto j_tag, int t) {
+  // Step t uses stage t % 4 (J below). Only the ragged last tile (kMasked) sets the
+  // P of keys >= N to zero; in every other tile all 32 keys are inside N. (A padded
+  // key's K row is zero, so its dS would add nothing to dQ anyway, but its P =
+  // exp2(-LSE2) could overflow for rows whose LSE is very negative, and 0 * inf is
+  // not 0.)
+  auto step = [&](auto j_tag, auto masked_tag, int t) {
     constexpr int J = decltype(j_tag)::value;
+    constexpr bool kMasked = decltype(masked_tag)::value;
     constexpr unsigned KT = J * kStage, VT = KT + kTile;
     issue(t + kStages - 1, lds + (unsigned)(((J + kStages - 1) % kStages) * kStage));
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
@@ -332,8 +337,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
     float ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = t * 32 + acc_row(i, g);
-      const float p = key < N ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq)) : 0.0f;
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq));
+      if constexpr (kMasked) {
+        if (t * 32 + acc_row(i, g) >= N) p = 0.0f;
+      }
       ds[i] = p * (dp[i] - dd);
     }
     const bf16x8_t b0 = pack8(ds), b1 = pack8(ds + 8);
@@ -353,16 +360,27 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  using Full = std::false_type;
+  using Ragged = std::true_type;
+  const int TF = N / 32;  // tiles with all 32 keys inside N
   int t = 0;
-  for (; t + kStages <= T; t += kStages) {
-    step(I0{}, t);
-    step(I1{}, t + 1);
-    step(I2{}, t + 2);
-    step(I3{}, t + 3);
+  for (; t + kStages <= TF; t += kStages) {
+    step(I0{}, Full{}, t);
+    step(I1{}, Full{}, t + 1);
+    step(I2{}, Full{}, t + 2);
+    step(I3{}, Full{}, t + 3);
   }
-  if (t < T) step(I0{}, t);
-  if (t + 1 < T) step(I1{}, t + 1);
-  if (t + 2 < T) step(I2{}, t + 2);
+  if (t < TF) step(I0{}, Full{}, t);
+  if (t + 1 < TF) step(I1{}, Full{}, t + 1);
+  if (t + 2 < TF) step(I2{}, Full{}, t + 2);
+  if (TF < T) {  // the ragged last tile, in stage TF % 4
+    switch (TF & 3) {
+      case 0: step(I0{}, Ragged{}, TF); break;
+      case 1: step(I1{}, Ragged{}, TF); break;
+      case 2: step(I2{}, Ragged{}, TF); break;
+      default: step(I3{}, Ragged{}, TF); break;
+    }
+  }
   // Loads issued past the last tile (zero fills) must land before the workgroup's
   // LDS can be handed to another workgroup.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
