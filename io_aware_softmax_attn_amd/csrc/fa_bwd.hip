@@ -109,28 +109,6 @@ __device__ __forceinline__ bf16x8_t pack8(const float* x) {
                                                   __builtin_bit_cast(unsigned, p2), __builtin_bit_cast(unsigned, p3)});
 }
 
-// Transposing read of a 32 x 32 block of a row-major LDS tile: lane l receives the
-// 8 values of column c0 + l%32 in rows r0 + 8g .. r0 + 8g + 7 (g = l/32), the A
-// operand of a product that contracts over those rows. r0 is a multiple of 16.
-template <int D>
-__device__ __forceinline__ bf16x8_t read_tr(unsigned tile, int r0, int c0, int lane) {
-  const int g = lane >> 5;
-  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int row = r0 + 8 * g + ((lane & 15) >> 2);
-  const unsigned a0 = tile + chunk_offset<D>(row, col >> 3) + 2 * (col & 7);
-  const unsigned a1 = tile + chunk_offset<D>(row + 4, col >> 3) + 2 * (col & 7);
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)a0);
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)a1);
-  return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5,
-                                 6, 7);
-}
-
-// Row-operand read: lane l receives chunk (2*ks + g) of tile row pi(l % 32).
-template <int D>
-__device__ __forceinline__ bf16x8_t read_row(unsigned tile, int ks, int lane) {
-  return *(const LDS_AS bf16x8_t*)(uintptr_t)(tile + chunk_offset<D>(pi_row(lane & 31), 2 * ks + (lane >> 5)));
-}
-
 // Workgroup id -> logical tile id such that each XCD (ids w with w % 8 == x) gets
 // a contiguous range: a head's tiles share one L2.
 __device__ __forceinline__ int remap_xcd(int w, int total) {
@@ -481,10 +459,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
       dma4(r, (unsigned)lane * 4u, __builtin_amdgcn_readfirstlane(st + (unsigned)(2 * kTile + wave * 256)));
     }
   };
-  // Per-lane LDS addresses of the operand reads for a stage at offset 0: the row
-  // reads of k-step ks (as read_row) and the two halves of the transposing reads of
-  // column block db (as read_tr with r0 = 0; r0 = 16 is 16 rows further, the swizzle
-  // depending on row bits 0-3 only). The loop below is unrolled over the four stages
+  // Per-lane LDS addresses of the operand reads for a stage at offset 0:
+  //  * row reads: for k-step ks, lane l receives chunk 2*ks + g of tile row
+  //    pi(l % 32), the row operand of a product that contracts over d;
+  //  * transposing reads (ds_read_b64_tr_b16): for column block db, lane l receives
+  //    the 8 values of column db*32 + l%32 in rows 8g .. 8g+7, as two reads of four
+  //    rows each: the A operand of a product that contracts over those rows. Rows
+  //    16-31 are 16 rows further, the swizzle depending on row bits 0-3 only.
+  // The loop below is unrolled over the four stages
   // of the ring, so every stage offset is a constant and rides in the ds_read
   // immediate (at most 3 * kStage + kTile + 16 rows < 64 KiB): no address
   // arithmetic per read. The empty asm keeps the compiler from recomputing them.
