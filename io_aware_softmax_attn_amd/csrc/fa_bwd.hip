@@ -526,6 +526,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
     const LDS_AS float* l2v = (const LDS_AS float*)(uintptr_t)(lds + CUR + 2 * kTile);
     const LDS_AS float* dvv = l2v + 64;
     float p[16], ds[16];
+    // LSE2 and D of the four softmax parts' rows, read at the step start.
+    f32x4_t l4s[4], d4s[4];
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      const int r = acc_row(4 * part, g);
+      l4s[part] = *(const LDS_AS f32x4_t*)(l2v + r);
+      d4s[part] = *(const LDS_AS f32x4_t*)(dvv + r);
+    }
     bf16x8_t rq[KS], rd[KS];  // row operands of tile t+1; only a window is live at once
 #pragma unroll
     for (int ks = 0; ks < kPer; ++ks) {
@@ -542,12 +550,10 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
           rd[ks] = rd_row(NXT + kTile, ks);
         }
       }
-#pragma unroll
-      for (int ks = part * kPer; ks < (part + 1) * kPer; ++ks) sdp_step(ks, rq[ks], rd[ks], s2, dp2);
-      // Softmax of rows acc_row(4*part, g) .. +3 of tile t.
-      const int r = acc_row(4 * part, g);
-      const f32x4_t l4 = *(const LDS_AS f32x4_t*)(l2v + r);
-      const f32x4_t d4 = *(const LDS_AS f32x4_t*)(dvv + r);
+      // Softmax of rows acc_row(4*part, g) .. +3 of tile t, spread over this part's
+      // 2*kPer product slots: each slot issues one MFMA, then the fma, exp2, sub and
+      // mul of its elements, which run on the VALU while the MFMA does. A fence
+      // closes each slot so the compiler cannot gather the VALU work in one place.
       float sx[4], dx[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -556,11 +562,24 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
       }
       asm volatile("" : "+v"(sx[0]), "+v"(sx[1]), "+v"(sx[2]), "+v"(sx[3]), "+v"(dx[0]), "+v"(dx[1]), "+v"(dx[2]),
                    "+v"(dx[3]));
+      constexpr int kSlots = 2 * kPer;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * part + j;
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[j], c, -l4[j]));
-        ds[i] = p[i] * (dx[j] - d4[j]);
+      for (int m = 0; m < kSlots; ++m) {
+        const int ks = part * kPer + m / 2;
+        if (m % 2 == 0) {
+          if (ks == 0) mfma_sv0(s2, rq[ks], kf[ks]);
+          else mfma_sv(s2, rq[ks], kf[ks]);
+        } else {
+          if (ks == 0) mfma_sv0(dp2, rd[ks], vf[ks]);
+          else mfma_sv(dp2, rd[ks], vf[ks]);
+        }
+#pragma unroll
+        for (int j = m * 4 / kSlots; j < (m + 1) * 4 / kSlots; ++j) {
+          const int i = 4 * part + j;
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[j], c, -l4s[part][j]));
+          ds[i] = p[i] * (dx[j] - d4s[part][j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       asm volatile("" : "+v"(p[4 * part]), "+v"(p[4 * part + 1]), "+v"(p[4 * part + 2]), "+v"(p[4 * part + 3]),
                    "+v"(ds[4 * part]), "+v"(ds[4 * part + 1]), "+v"(ds[4 * part + 2]), "+v"(ds[4 * part + 3]));
