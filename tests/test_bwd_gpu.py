@@ -66,7 +66,9 @@ def run_bwd(fa, q, k, v, dO, scale):
 
 
 CASES = [(1, 1, 64, 64, 1, 1.0), (1, 2, 300, 128, 2, 1.0), (2, 3, 1000, 64, 3, 1.0), (1, 1, 1, 128, 4, 1.0),
-         (1, 2, 129, 128, 5, 2.5), (1, 4, 2048, 128, 6, 1.0), (2, 1, 777, 64, 7, 2.5)]
+         (1, 2, 129, 128, 5, 2.5), (1, 4, 2048, 128, 6, 1.0), (2, 1, 777, 64, 7, 2.5),
+         # ragged last key tile in each position of the four-stage ring (full tiles mod 4 = 2, 3)
+         (1, 2, 327, 128, 8, 1.0), (1, 1, 69, 64, 9, 2.5), (1, 1, 97, 128, 10, 1.0)]
 
 
 @pytest.mark.parametrize("B,H,N,d,seed,sigma", CASES)
