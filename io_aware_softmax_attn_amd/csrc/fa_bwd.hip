@@ -607,9 +607,12 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
     }
     // Tile t+2 (read from step t+1 on) has landed; tile t+3 may stay in flight.
     tile_barrier<kPerTile>();
-    // The products of S2 and dP2 were issued before the 4*DB accumulator products;
-    // the pin still covers the wait states before the VALU reads them.
-    sync_sv(s2, dp2);
+    // The products of S2 and dP2 were issued before the 4*DB accumulator products,
+    // which issue in order behind them on the same matrix core, so their results are
+    // written long before the next step's VALU reads them; the s_nop adds the two
+    // wait states of a VALU read after an MFMA issue, and the pin keeps those reads
+    // after this point.
+    asm volatile("s_nop 1" : "+v"(s2), "+v"(dp2));
   };
 #pragma unroll
   for (int u = 0; u < kStages - 1; ++u) {
