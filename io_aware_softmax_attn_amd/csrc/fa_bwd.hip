@@ -305,13 +305,15 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
     constexpr int J = decltype(j_tag)::value;
     constexpr bool kMasked = decltype(masked_tag)::value;
     constexpr unsigned KT = J * kStage, VT = KT + kTile;
-    issue(t + kStages - 1, lds + (unsigned)(((J + kStages - 1) % kStages) * kStage));
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s = mfma(rd_row(KT, ks), qf[ks], s);
       dp = mfma(rd_row(VT, ks), df[ks], dp);
     }
+    // Issued after the S/dP reads, so those start right after the barrier (the
+    // loads' asm is a compiler memory fence).
+    issue(t + kStages - 1, lds + (unsigned)(((J + kStages - 1) % kStages) * kStage));
     float ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
