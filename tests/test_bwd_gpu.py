@@ -83,6 +83,20 @@ def test_bwd_parity(fa, B, H, N, d, seed, sigma):
         assert err[n] <= 2.0 * unf[n] + 1e-6, (n, err[n], unf[n])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [2, 5, 16, 31, 32, 33, 48, 63, 65, 95, 96, 100, 127, 128, 130, 160, 161, 191, 193, 250])
+def test_bwd_short_lengths(fa, d, N):
+    """Short and ragged sequences: few 32-row or 32-key tiles, so the kernels run
+    only (or mostly) the remainder steps of their loops unrolled over the ring."""
+    announce(f"bwd short N={N} d={d}")
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, dO = make_case(1, 2, N, d, 300 + N + d)
+    grads = run_bwd(fa, q, k, v, dO, scale)
+    err, unf = bwd_errors(q, k, v, dO, grads, scale)
+    for n in NAMES:
+        assert err[n] <= 2.0 * unf[n] + 1e-6, (N, d, n, err[n], unf[n])
+
+
 def test_bwd_parity_full_size_sampled_heads(fa):
     """The benchmark shape, B=1 H=32 N=8192 d=128: two sampled heads against the oracle."""
     announce("bwd B=1 H=32 N=8192 d=128, heads 0 and 31")
