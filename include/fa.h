@@ -65,7 +65,8 @@ typedef enum {
  * One kernel launch: Q is tiled by rows, K/V stream through on-chip memory in
  * column tiles, and the online softmax (running max, running sum, rescaled
  * accumulator; "Flash Attention (FA1)", derivation steps 1-5) keeps S and P on
- * chip. O is rounded to bf16 (nearest-even) once, at the end.
+ * chip. O is rounded to bf16 (nearest-even) once, at the end. The query-tile
+ * height is the one fa_select_blocks returns for the shape.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, void* stream);
