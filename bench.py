@@ -594,6 +594,8 @@ def main():
                          "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin")
     ap.add_argument("--tile-order", type=int, default=0, choices=(0, 1, 2),
                     help="fused path only: workgroup-to-tile order of fa_fwd_tile_order (0 = fa_fwd's)")
+    ap.add_argument("--all", action="store_true",
+                    help="one JSON line per named forward workload (the benchmark line is the default run's)")
     ap.add_argument("--br", type=int, default=0, choices=(0, 128, 256),
                     help="fused path only: query rows per workgroup (fa_fwd_blocks); 0 = the selector's choice")
     ap.add_argument("--shape", metavar="B,H,N,d",
@@ -641,7 +643,20 @@ def main():
     if args.backward:
         backward_bench(args)
         return
+    if args.all:
+        import attn_inputs
 
+        args.no_cpu_baseline = True
+        for w in attn_inputs.WORKLOADS:
+            args.workload = w.name
+            fused_bench(args)
+        return
+    fused_bench(args)
+
+
+def fused_bench(args):
+    """Time the fused forward (or, with --unfused, the three-kernel baseline) on one
+    workload and print its JSON line."""
     import torch
 
     import attn_inputs
