@@ -383,7 +383,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
 
 // ---- kernel 3: dK and dV ----
 // Two waves per SIMD at d = 64; at d = 128 the two d x 32 accumulators, K and V
-// (about 330 registers) leave room for one.
+// (192 AGPRs) and about 160 VGPRs leave room for one.
 template <int D>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                        const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
@@ -514,12 +514,13 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
   // and dP of tile t+1, and tiles t+2 and t+3 are in flight from memory: tile t+3's
   // loads go out during step t into the stage that tile t-1 used (its last reads
   // were consumed by step t-1's products, before the barrier ending that step), and
-  // the barrier ending step t+1 waits for them. The softmax is cut into four parts
-  // placed between the product pairs, each pinned to its place (inputs at its start,
-  // outputs at its end) so the VALU work interleaves with the MFMAs instead of
-  // running before them. Tiles past the end are zero rows, so every step runs the
-  // same code. Step t uses stage t % 4 (J below); S and dP alternate between two
-  // register sets, so no copy is needed between steps.
+  // the barrier ending step t+1 waits for them. The softmax is cut into four parts,
+  // one per group of S/dP products, and within a part each product slot carries the
+  // VALU work of one or two elements, so that work runs beside the MFMAs. Each part
+  // is pinned to its place (inputs at its start, outputs at its end). Tiles past
+  // the end are zero rows, so every step runs the same code. Step t uses stage
+  // t % 4 (J below); S and dP alternate between two register sets, so no copy is
+  // needed between steps.
   constexpr int kPer = KS / 4;
   auto step = [&](auto j_tag, int t, f32x16_t& s, f32x16_t& dp, f32x16_t& s2, f32x16_t& dp2) {
     constexpr int J = decltype(j_tag)::value;
