@@ -393,7 +393,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D, NQB>& w, int j, int T, int
   if constexpr (kPV) {
     // The previous softmax moved the reference max (uniform branch, rarely
     // taken): bring the PV products accumulated so far to the new reference.
-    if (w.rescale) {
+    if (__builtin_expect(w.rescale, false)) {
       sync_acc_all(w.acc);
       // One fragment at a time: each asm ties the finished fragment to the next
       // one, so the compiler cannot pull all of them into VGPRs at once.
@@ -618,7 +618,7 @@ __device__ __forceinline__ void pipeline_step(Wave<D, NQB>& w, int j, int T, int
   };
   auto finish_softmax = [&]() {
     if constexpr (kExp) {
-      if (big_rows != 0) {
+      if (__builtin_expect(big_rows != 0, false)) {
         float alpha[NQB];
         move_reference<kMasked>(scur, w.m, w.l, alpha, c, nv8);
 #pragma unroll
