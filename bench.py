@@ -223,9 +223,9 @@ def summarize_io_sweep(sweep_dir, copy_bytes):
         "(or BR), length and counter:",
         "",
         "```",
-        IO_SWEEP_CMD.format(ctr="<FETCH_SIZE|WRITE_SIZE>", dir="gpurun_out/io_sweep", order="<order>", n="<N>",
+        IO_SWEEP_CMD.format(ctr="<FETCH_SIZE|WRITE_SIZE>", dir=sweep_dir.rstrip("/"), order="<order>", n="<N>",
                             B=B, H=H, d=d),
-        IO_SWEEP_BR_CMD.format(ctr="<FETCH_SIZE|WRITE_SIZE>", dir="gpurun_out/io_sweep", n="<N>", B=B, H=H, d=d),
+        IO_SWEEP_BR_CMD.format(ctr="<FETCH_SIZE|WRITE_SIZE>", dir=sweep_dir.rstrip("/"), n="<N>", B=B, H=H, d=d),
         "```",
         "",
         "Models: `once` = B*H*N*(8d+4) (Q, K, V read once, O and LSE written once); `re-read` = K and V "
