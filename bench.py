@@ -9,9 +9,14 @@ in HBM before the timed region. Prints ONE JSON line.
   python bench.py --memory OUT_MD      (peak device memory, fused vs unfused)
   python bench.py --decode [--workload dec_...]   (decode-shaped forward, GB/s)
   python bench.py --backward [--workload NAME]    (backward dQ, dK, dV, TFLOP/s)
+  python bench.py --all [--eager]      (one line per named forward workload)
 
-The roofline entry is measured live: per-launch HIP events recorded on the stream
-the kernel runs on, averaged over the timed region. Its ``traffic`` field comes
+The K timed launches of the fused forward are captured once in a HIP graph and
+replayed between two HIP events on the stream they run on; the average launch
+duration is the replay time over K. --eager launches them one by one from Python
+instead, each between its own pair of events: that adds the event packets and the
+dispatch latency to every launch (about 20 us, 2.5% at the benchmark workload)
+and, for short launches, the host's per-call cost. The ``traffic`` field comes
 from the committed rocprofv3 counter summary of the same kernel
 (profiles/fa_fwd_*_traffic.json) when its recorded source hash still matches the
 kernel source, else null. The CPU baseline times the fp64 oracle on the host
@@ -244,7 +249,7 @@ def summarize_io_sweep(sweep_dir, copy_bytes):
     print("\n".join(lines))
 
 
-def summarize_trace(stats_csv, command, workload):
+def summarize_trace(stats_csv, command, workload, steps=50):
     """Write the per-kernel duration summary of a rocprofv3 --stats run, with the
     command that produced it and the algorithmic rate at the average duration."""
     import csv
@@ -283,8 +288,21 @@ def summarize_trace(stats_csv, command, workload):
         avg_s = float(r["AverageNs"]) * 1e-9
         tf = w.flops / avg_s / 1e12
         lines += ["", f"Fused kernel at its average duration: {w.flops:.4e} FLOP per launch -> {tf:.1f} TFLOP/s, "
-                      f"{tf / MFMA_BF16_PEAK_TFLOPS:.4f} of the {MFMA_BF16_PEAK_TFLOPS} TFLOP/s bf16 MFMA peak.",
-                  f"Kernel source sha256[:16] of fa_fwd.hip: {kernel_source_hash()}."]
+                      f"{tf / MFMA_BF16_PEAK_TFLOPS:.4f} of the {MFMA_BF16_PEAK_TFLOPS} TFLOP/s bf16 MFMA peak "
+                      "(the average over every launch, warmup included)."]
+        # The per-dispatch trace next to the stats file: the last `steps` launches are
+        # the timed region, the span that bench.py's own events measure.
+        trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
+        if trace_csv != stats_csv and os.path.exists(trace_csv):
+            disp = sorted((t for t in csv.DictReader(open(trace_csv)) if "fa_fwd_kernel" in t["Kernel_Name"]),
+                          key=lambda t: int(t["Start_Timestamp"]))[-steps:]
+            durs = [(int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) * 1e-3 for t in disp]
+            gaps = [(int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) * 1e-3 for a, b in zip(disp, disp[1:])]
+            mean = sum(durs) / len(durs)
+            lines.append(f"The last {len(disp)} launches (the timed region): {mean:.1f} us per kernel on average "
+                         f"(min {min(durs):.1f}, max {max(durs):.1f}), {sum(gaps) / max(len(gaps), 1):.2f} us "
+                         f"between kernels on average -> {w.flops / (mean * 1e-6) / 1e12:.1f} TFLOP/s.")
+        lines.append(f"Kernel source sha256[:16] of fa_fwd.hip: {kernel_source_hash()}.")
     if decode:
         split = [r for r in rows if any(kname in r["Name"] for kname in DECODE_KERNELS)]
         total_s = sum(float(r["AverageNs"]) for r in split) * 1e-9
@@ -594,6 +612,9 @@ def main():
                          "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin")
     ap.add_argument("--tile-order", type=int, default=0, choices=(0, 1, 2),
                     help="fused path only: workgroup-to-tile order of fa_fwd_tile_order (0 = fa_fwd's)")
+    ap.add_argument("--eager", action="store_true",
+                    help="fused path: time each launch between its own pair of events instead of one "
+                         "replay of the K launches captured in a HIP graph")
     ap.add_argument("--all", action="store_true",
                     help="one JSON line per named forward workload (the benchmark line is the default run's)")
     ap.add_argument("--br", type=int, default=0, choices=(0, 128, 256),
@@ -612,6 +633,8 @@ def main():
                     help="instead of timing: peak device memory of the fused and unfused forward over "
                          "a range of sequence lengths, written as a table to OUT_MD")
     args = ap.parse_args()
+    if args.eager and (args.unfused or args.backward or args.decode or args.memory):
+        ap.error("--eager applies to the fused forward only")
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_calibration,
@@ -621,7 +644,7 @@ def main():
         summarize_io_sweep(args.summarize_io_sweep, args.copy_calibration)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload)
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload, args.steps)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -684,30 +707,51 @@ def fused_bench(args):
         torch.cuda.synchronize()
         del src, dst
 
-    def launch():
+    def launch(s=stream):
         if args.unfused:
-            fa.fa_unfused_fwd(qg, kg, vg, o, lse, ws, scale=w.scale, stream=stream)
+            fa.fa_unfused_fwd(qg, kg, vg, o, lse, ws, scale=w.scale, stream=s)
         elif args.tile_order:
-            fa.fa_fwd_tile_order(qg, kg, vg, o, lse, args.tile_order, scale=w.scale, stream=stream)
+            fa.fa_fwd_tile_order(qg, kg, vg, o, lse, args.tile_order, scale=w.scale, stream=s)
         elif args.br:
-            fa.fa_fwd_blocks(qg, kg, vg, o, lse, args.br, scale=w.scale, stream=stream)
+            fa.fa_fwd_blocks(qg, kg, vg, o, lse, args.br, scale=w.scale, stream=s)
         else:
-            fa.fa_fwd(qg, kg, vg, o, lse, scale=w.scale, stream=stream)
+            fa.fa_fwd(qg, kg, vg, o, lse, scale=w.scale, stream=s)
 
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        launch()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    # The unfused baseline and the counter runs (--launches-only) launch eagerly.
+    use_graph = not (args.eager or args.unfused or args.launches_only)
+    if use_graph:
+        # The K launches captured once into a HIP graph (the library allocates and
+        # clears nothing, so every launch records as a plain kernel node) and replayed
+        # under one pair of events: no host work between the launches.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(args.steps):
+                launch(None)  # torch's current stream is the capture stream here
+        g.replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_launch_ms = [start.elapsed_time(end) / args.steps]
+    else:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            starts[i].record(stream)
+            launch()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = sum(per_launch_ms) / len(per_launch_ms)
     step_ms = max(wall * 1e3 / args.steps, avg_ms)
 
@@ -729,7 +773,8 @@ def fused_bench(args):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False,
                    "path": "unfused-3-kernel" if args.unfused else "fused",
                    **({} if args.unfused else {"br": args.br or fa.fa_select_blocks(w.d, w.N, w.B, w.H)[0]}),
-                   **({"tile_order": args.tile_order} if args.tile_order else {})},
+                   **({"tile_order": args.tile_order} if args.tile_order else {}),
+                   "launch": "graph" if use_graph else "eager"},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
@@ -738,7 +783,7 @@ def fused_bench(args):
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
             "kernel_ms_avg": round(avg_ms, 4),
-            "kernel_ms_min": round(min(per_launch_ms), 4),
+            "kernel_ms_min": None if use_graph else round(min(per_launch_ms), 4),
             "flops_per_launch": w.flops,
             "min_hbm_bytes_per_launch": w.min_hbm_bytes,
             # HBM rate of the counted bytes over the average launch, against the 8 TB/s roofline
