@@ -354,6 +354,38 @@ def decode_cpu_baseline(w, q, k, v, target_s: float = 10.0):
     }
 
 
+def time_launches(torch, launch, steps, stream, use_graph):
+    """Run `steps` timed launches of `launch(stream)` and return (per-launch ms list,
+    wall seconds). With use_graph, the launches are captured once in a HIP graph
+    (launched on torch's capture stream), replayed once untimed, then replayed once
+    between two events on `stream`: the list holds the replay time over `steps`.
+    Otherwise each launch is issued eagerly between its own pair of events."""
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                launch(None)  # torch's current stream is the capture stream here
+        g.replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return [start.elapsed_time(end) / steps], time.perf_counter() - t0
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        launch(stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in zip(starts, ends)], wall
+
+
 def decode_bench(args):
     """Time the decode-shaped forward (split + merge kernels) and print one JSON line."""
     import torch
@@ -381,16 +413,10 @@ def decode_bench(args):
     for _ in range(args.warmup):
         fa.fa_decode_fwd(qg, kg, vg, o, lse, ws, scale=w.scale, stream=stream)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        fa.fa_decode_fwd(qg, kg, vg, o, lse, ws, scale=w.scale, stream=stream)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    use_graph = not (args.eager or args.launches_only)
+    per_ms, wall = time_launches(
+        torch, lambda s: fa.fa_decode_fwd(qg, kg, vg, o, lse, ws, scale=w.scale, stream=s), args.steps, stream,
+        use_graph)
     avg_ms = sum(per_ms) / len(per_ms)
     gbs = w.min_hbm_bytes / (avg_ms * 1e-3) / 1e9
     line = {
@@ -407,7 +433,8 @@ def decode_bench(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "splits": splits, "chunk": chunk, "path": "decode split+merge"},
+                   "splits": splits, "chunk": chunk, "path": "decode split+merge",
+                   "launch": "graph" if use_graph else "eager"},
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbs, 1),
@@ -416,7 +443,7 @@ def decode_bench(args):
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": load_traffic(w.name, "fa_decode", DECODE_SRC),
             "kernel_ms_avg": round(avg_ms, 4),
-            "kernel_ms_min": round(min(per_ms), 4),
+            "kernel_ms_min": None if use_graph else round(min(per_ms), 4),
             "min_hbm_bytes_per_launch": w.min_hbm_bytes,
             "tflops": round(w.flops / (avg_ms * 1e-3) / 1e12, 2),
         },
@@ -457,16 +484,10 @@ def backward_bench(args):
     for _ in range(args.warmup):
         fa.fa_bwd(qg, kg, vg, o, lse, gg, dq, dk, dv, ws, scale=w.scale, stream=stream)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        fa.fa_bwd(qg, kg, vg, o, lse, gg, dq, dk, dv, ws, scale=w.scale, stream=stream)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    use_graph = not (args.eager or args.launches_only)
+    per_ms, wall = time_launches(
+        torch, lambda s: fa.fa_bwd(qg, kg, vg, o, lse, gg, dq, dk, dv, ws, scale=w.scale, stream=s), args.steps,
+        stream, use_graph)
     avg_ms = sum(per_ms) / len(per_ms)
     flops = 2.5 * w.flops
     tf = flops / (avg_ms * 1e-3) / 1e12
@@ -483,7 +504,8 @@ def backward_bench(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False, "path": "backward"},
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False, "path": "backward",
+                   "launch": "graph" if use_graph else "eager"},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tf, 2),
@@ -492,7 +514,7 @@ def backward_bench(args):
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None,
             "kernel_ms_avg": round(avg_ms, 4),
-            "kernel_ms_min": round(min(per_ms), 4),
+            "kernel_ms_min": None if use_graph else round(min(per_ms), 4),
             "flops_per_launch": flops,
             "executed_flops_per_launch": 3.5 * w.flops,
         },
@@ -613,8 +635,8 @@ def main():
     ap.add_argument("--tile-order", type=int, default=0, choices=(0, 1, 2),
                     help="fused path only: workgroup-to-tile order of fa_fwd_tile_order (0 = fa_fwd's)")
     ap.add_argument("--eager", action="store_true",
-                    help="fused path: time each launch between its own pair of events instead of one "
-                         "replay of the K launches captured in a HIP graph")
+                    help="time each launch between its own pair of events instead of one replay of the K "
+                         "launches captured in a HIP graph (fused forward, --backward, --decode)")
     ap.add_argument("--all", action="store_true",
                     help="one JSON line per named forward workload (the benchmark line is the default run's)")
     ap.add_argument("--br", type=int, default=0, choices=(0, 128, 256),
@@ -633,8 +655,8 @@ def main():
                     help="instead of timing: peak device memory of the fused and unfused forward over "
                          "a range of sequence lengths, written as a table to OUT_MD")
     args = ap.parse_args()
-    if args.eager and (args.unfused or args.backward or args.decode or args.memory):
-        ap.error("--eager applies to the fused forward only")
+    if args.eager and (args.unfused or args.memory):
+        ap.error("--eager applies to the fused forward, --backward and --decode")
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.copy_calibration,
@@ -721,37 +743,11 @@ def fused_bench(args):
         launch()
     torch.cuda.synchronize()
 
-    # The unfused baseline and the counter runs (--launches-only) launch eagerly.
+    # The library allocates and clears nothing, so every launch records into the graph
+    # as plain kernel nodes. The unfused baseline and the counter runs
+    # (--launches-only) launch eagerly.
     use_graph = not (args.eager or args.unfused or args.launches_only)
-    if use_graph:
-        # The K launches captured once into a HIP graph (the library allocates and
-        # clears nothing, so every launch records as a plain kernel node) and replayed
-        # under one pair of events: no host work between the launches.
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(args.steps):
-                launch(None)  # torch's current stream is the capture stream here
-        g.replay()
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        start.record(stream)
-        g.replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per_launch_ms = [start.elapsed_time(end) / args.steps]
-    else:
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            starts[i].record(stream)
-            launch()
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    per_launch_ms, wall = time_launches(torch, launch, args.steps, stream, use_graph)
     avg_ms = sum(per_launch_ms) / len(per_launch_ms)
     step_ms = max(wall * 1e3 / args.steps, avg_ms)
 
