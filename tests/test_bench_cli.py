@@ -29,3 +29,30 @@ def test_summarize_trace_needs_no_gpu(tmp_path):
     out = (tmp_path / "profiles" / "fa_unfused_b1h32_n8192_d128_kernel_trace.md").read_text()
     assert "`unf_qk_kernel<128>` | 2 | 100.0 |" in out
     assert "python3 bench.py --unfused" in out
+
+
+def test_summarize_trace_reports_the_timed_launches(tmp_path):
+    """With the per-dispatch trace next to the stats CSV, the fused summary also
+    gives the average duration of the last `steps` launches and the gaps between
+    them; the earlier (warmup) launches do not enter it."""
+    name = "_ZN2fa12_GLOBAL__N_113fa_fwd_kernelILi128ELi2EEEvPKDF16b"
+    (tmp_path / "fa_kernel_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        f'"{name}",5,5000000,1000000.0,100.0,800000,1400000,1.0\n')
+    rows = ['"Kernel_Name","Start_Timestamp","End_Timestamp"']
+    t = 0
+    for dur, gap in ((1400000, 0), (1000000, 0), (800000, 10000), (800000, 20000), (1000000, 0)):
+        rows.append(f'"{name}",{t},{t + dur}')
+        t += dur + gap
+    (tmp_path / "fa_kernel_trace.csv").write_text("\n".join(rows) + "\n")
+    (tmp_path / "profiles").mkdir()
+    r = subprocess.run([sys.executable, "-c",
+                        "import sys, bench; bench.ROOT = sys.argv[1]; "
+                        "bench.summarize_trace(sys.argv[2], 'rocprofv3 ... -- python3 bench.py', None, 3)",
+                        str(tmp_path), str(tmp_path / "fa_kernel_stats.csv")],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    out = (tmp_path / "profiles" / "fa_fwd_b1h32_n8192_d128_kernel_trace.md").read_text()
+    # last three: 800, 800, 1000 us -> 866.7 us; gaps between them 10 and 20 us -> 15 us
+    assert "The last 3 launches (the timed region): 866.7 us per kernel on average (min 800.0, max 1000.0), " \
+           "15.00 us between kernels" in out
