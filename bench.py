@@ -41,6 +41,12 @@ METRIC = "fwd attention TFLOP/s & % of bf16 MFMA peak, B=1 H=32 N=8192 d=128"
 KERNEL_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_fwd.hip")
 UNFUSED_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_unfused.hip")
 DECODE_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_decode.hip")
+
+
+def metric_for(metric, shape):
+    """The metric name with its trailing shape replaced by `shape` (the name as given
+    when the shape is the one it is quoted on)."""
+    return metric.rsplit(", ", 1)[0] + ", " + shape
 DECODE_METRIC = "decode attention GB/s (Q, K, V read and O, LSE written once) & % of HBM peak, " \
                 "B=16 H=32 Nq=1 Nk=8192 d=128"
 
@@ -420,7 +426,7 @@ def decode_bench(args):
     avg_ms = sum(per_ms) / len(per_ms)
     gbs = w.min_hbm_bytes / (avg_ms * 1e-3) / 1e9
     line = {
-        "metric": DECODE_METRIC,
+        "metric": metric_for(DECODE_METRIC, f"B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d}"),
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -492,7 +498,7 @@ def backward_bench(args):
     flops = 2.5 * w.flops
     tf = flops / (avg_ms * 1e-3) / 1e12
     line = {
-        "metric": BWD_METRIC,
+        "metric": metric_for(BWD_METRIC, f"B={w.B} H={w.H} N={w.N} d={w.d}"),
         "value": round(tf, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -754,7 +760,7 @@ def fused_bench(args):
     tflops = w.flops / (avg_ms * 1e-3) / 1e12
     traffic = None if (args.unfused or args.br or args.tile_order) else load_traffic(w.name)
     line = {
-        "metric": METRIC,
+        "metric": metric_for(METRIC, f"B={w.B} H={w.H} N={w.N} d={w.d}"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -56,3 +56,14 @@ def test_summarize_trace_reports_the_timed_launches(tmp_path):
     # last three: 800, 800, 1000 us -> 866.7 us; gaps between them 10 and 20 us -> 15 us
     assert "The last 3 launches (the timed region): 866.7 us per kernel on average (min 800.0, max 1000.0), " \
            "15.00 us between kernels" in out
+
+
+def test_metric_names_the_shape_it_measures():
+    """The default lines carry the metric names as quoted (their shapes are the
+    benchmark shapes); other workloads carry their own shape in the name."""
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.metric_for(bench.METRIC, "B=1 H=32 N=8192 d=128") == bench.METRIC
+    assert bench.metric_for(bench.BWD_METRIC, "B=1 H=32 N=8192 d=128") == bench.BWD_METRIC
+    assert bench.metric_for(bench.DECODE_METRIC, "B=16 H=32 Nq=1 Nk=8192 d=128") == bench.DECODE_METRIC
+    assert bench.metric_for(bench.METRIC, "B=4 H=16 N=1024 d=64").endswith(", B=4 H=16 N=1024 d=64")
