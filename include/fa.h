@@ -20,8 +20,9 @@
  *     a call returns.
  *   - d (head dimension) must be 64 or 128. B, H, N >= 0; when B*H*N == 0 the
  *     call is a no-op that returns FA_OK without touching any pointer.
- *   - scale must be finite and >= 0 (the pages' scale is 1/sqrt(d) > 0; 0 gives
- *     the uniform average).
+ *   - scale must be finite, of either sign (the pages' scale is 1/sqrt(d) > 0; 0
+ *     gives the uniform average; a negative scale is the softmax of the negated
+ *     scores, which the running max handles like any other).
  *   - Q, K, V, O must be 16-byte aligned; LSE 4-byte aligned. Q, K and V may
  *     share memory; O and LSE must not overlap any input or each other.
  *   - Work is launched on the calling thread's current HIP device; the tensors
@@ -50,7 +51,7 @@ typedef enum {
   FA_ERR_SHAPE = -2,     /* B, H or N negative; decode: Nq or Nk out of range */
   FA_ERR_HEADDIM = -3,   /* d not in {64, 128} */
   FA_ERR_ALIGN = -4,     /* a pointer is not aligned as stated above */
-  FA_ERR_SCALE = -5,     /* scale not finite or negative */
+  FA_ERR_SCALE = -5,     /* scale not finite */
   FA_ERR_ALIAS = -6,     /* O or LSE overlaps an input or each other */
   FA_ERR_OVERFLOW = -7,  /* sizes overflow 64-bit byte counts or the launch grid */
   FA_ERR_WORKSPACE = -8, /* workspace missing, too small, misaligned or overlapping */

@@ -51,6 +51,7 @@ class FaArgumentError(FaError, ValueError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_build.LIB_PATH):
         _build.build_library()
+    _build.check_built()  # a library left from older sources is never loaded
     dll = ctypes.CDLL(_build.LIB_PATH)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     dll.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp]

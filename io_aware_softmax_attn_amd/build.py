@@ -8,6 +8,7 @@ an atomic rename, so a half-written file is never loaded.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -18,7 +19,28 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 SOURCES = ["fa_fwd.hip", "fa_unfused.hip", "fa_decode.hip", "fa_bwd.hip", "fa_api.cpp", "fa_select.cpp"]
+HEADERS = [os.path.join(CSRC, "fa_internal.h"), os.path.join(os.path.dirname(PKG_DIR), "include", "fa.h")]
 ARCH = "gfx950"
+HASH_PATH = LIB_PATH + ".srchash"  # sha256 of the sources and flags libfa.so was built from
+
+
+def source_hash() -> str:
+    """sha256 over the compile flags and the bytes of every source and header."""
+    h = hashlib.sha256(" ".join(compile_command("libfa.so")[1:]).encode())
+    for path in [os.path.join(CSRC, s) for s in SOURCES] + HEADERS:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def check_built() -> None:
+    """Raise unless libfa.so exists and was built from the current sources."""
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing")
+    recorded = open(HASH_PATH).read().strip() if os.path.exists(HASH_PATH) else None
+    if recorded != source_hash():
+        raise RuntimeError(f"{LIB_PATH} was built from other sources than the current ones; rebuild it with "
+                           f"'python io_aware_softmax_attn_amd/build.py'")
 
 
 def hipcc() -> str:
@@ -31,7 +53,7 @@ def hipcc() -> str:
 def compile_command(out: str) -> list[str]:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        shutil.which("hipcc") or "/opt/rocm/bin/hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 VALU ops are kept out of generated code on this part
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",
@@ -40,6 +62,8 @@ def compile_command(out: str) -> list[str]:
 
 
 def build_library(verbose: bool = False) -> str:
+    hipcc()
+    digest = source_hash()
     fd, tmp = tempfile.mkstemp(prefix="libfa.", suffix=".so.tmp", dir=PKG_DIR)
     os.close(fd)
     try:
@@ -50,6 +74,8 @@ def build_library(verbose: bool = False) -> str:
         if res.returncode != 0:
             raise RuntimeError(f"building libfa.so failed (exit {res.returncode}): {' '.join(cmd)}")
         os.replace(tmp, LIB_PATH)
+        with open(HASH_PATH, "w") as f:
+            f.write(digest + "\n")
     finally:
         if os.path.exists(tmp):
             os.remove(tmp)

@@ -38,7 +38,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "B, H and N must be >= 0 (decode: 1 <= Nq <= 16 and 1 <= Nk <= 2^30)";
     case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
     case FA_ERR_ALIGN: return "q, k, v, o and workspace must be 16-byte aligned, lse 4-byte aligned";
-    case FA_ERR_SCALE: return "scale must be finite and >= 0";
+    case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_ALIAS: return "o or lse overlaps an input, or each other";
     case FA_ERR_OVERFLOW: return "problem size overflows 64-bit byte counts or the launch grid";
     case FA_ERR_WORKSPACE: return "workspace is missing, too small, misaligned or overlaps a tensor";
@@ -78,7 +78,7 @@ int fa_check_args(const void* q, const void* k, const void* v, const void* o, co
                   int need_workspace, const void* workspace, size_t workspace_bytes) {
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (!std::isfinite(scale) || scale < 0.0f) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
   // B, H, N < 2^31, so B*H < 2^62 and B*H*N cannot wrap once B*H < 2^33.
   if ((uint64_t)B * (uint64_t)H > (std::numeric_limits<uint64_t>::max() >> 31)) return FA_ERR_OVERFLOW;
   const uint64_t rows64 = (uint64_t)B * (uint64_t)H * (uint64_t)N;
@@ -131,7 +131,7 @@ int fa_decode_check_args(const void* q, const void* k, const void* v, const void
                          int Nq, int Nk, int d, float scale, const void* workspace, size_t workspace_bytes) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (!std::isfinite(scale) || scale < 0.0f) return FA_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
   if ((uint64_t)B * (uint64_t)H > (std::numeric_limits<uint64_t>::max() >> 31)) return FA_ERR_OVERFLOW;
   const uint64_t bh = (uint64_t)B * (uint64_t)H;
   const uint64_t rows64 = bh * (uint64_t)Nq;

@@ -316,23 +316,27 @@ struct Wave {
 };
 
 // Online-softmax reference update for one 32-key sub-tile (FA1 page, derivation
-// steps 1-2), the slow path: the row max of the sub-tile, a new reference max
-// m_new = max(m, rowmax) per row, alpha = exp2(m_old - m_new), and l rescaled.
-// kMasked sets keys >= nvalid (passed as nvalid - 8g) to -inf first.
+// steps 1-2), the slow path: the row max of the sub-tile's scaled scores, a new
+// reference max m_new = max(m, rowmax) per row, alpha = exp2(m_old - m_new), and l
+// rescaled. The max is taken over the scaled scores s * c, so that it is the max
+// of the softmax's arguments for a scale of either sign. kMasked leaves keys >=
+// nvalid (passed as nvalid - 8g) out of the max; the caller's exp2 stage zeroes
+// their terms.
 template <bool kMasked, int NQB>
-__device__ __forceinline__ void move_reference(f32x16_t (&s)[NQB], float (&m)[NQB], float (&l)[NQB],
+__device__ __forceinline__ void move_reference(const f32x16_t (&s)[NQB], float (&m)[NQB], float (&l)[NQB],
                                                float (&alpha)[NQB], float c, int nv8) {
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     float x = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      float t = s[qb][i] * c;
       if constexpr (kMasked) {
-        if (key_of_reg(i) >= nv8) s[qb][i] = -__builtin_inff();
+        if (key_of_reg(i) >= nv8) t = -__builtin_inff();
       }
-      x = fmaxf(x, s[qb][i]);
+      x = fmaxf(x, t);
     }
-    const float mn = fmaxf(m[qb], pair_max(x) * c);
+    const float mn = fmaxf(m[qb], pair_max(x));
     alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mn);
     m[qb] = mn;
     l[qb] *= alpha[qb];

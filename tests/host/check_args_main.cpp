@@ -82,7 +82,7 @@ int main() {
   EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, 0, sc, nullptr) == FA_ERR_HEADDIM);
   EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, std::nanf(""), nullptr) == FA_ERR_SCALE);
   EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, INFINITY, nullptr) == FA_ERR_SCALE);
-  EXPECT(fa_fwd(q, k, v, o, lse, B, H, N, d, -0.5f, nullptr) == FA_ERR_SCALE);
+  EXPECT(fa_check_args(q, k, v, o, lse, B, H, N, d, -0.5f, 0, nullptr, 0) == FA_OK);
   EXPECT(fa_fwd(q + 8, k, v, o, lse, B, H, N, d, sc, nullptr) == FA_ERR_ALIGN);
   EXPECT(fa_fwd(q, k, v, o + 2, lse, B, H, N, d, sc, nullptr) == FA_ERR_ALIGN);
   EXPECT(fa_fwd(q, k, v, o, reinterpret_cast<float*>(reinterpret_cast<char*>(lse) + 2), B, H, N, d, sc, nullptr) ==

@@ -105,7 +105,7 @@ def test_check_args_errors(fa):
     assert check(fa, d=256) == S["FA_ERR_HEADDIM"]
     assert check(fa, scale=float("nan")) == S["FA_ERR_SCALE"]
     assert check(fa, scale=float("inf")) == S["FA_ERR_SCALE"]
-    assert check(fa, scale=-0.5) == S["FA_ERR_SCALE"]
+    assert check(fa, scale=-0.5) == 0  # any finite scale: softmax of the negated scores
     assert check(fa, q=None) == S["FA_ERR_NULL"]
     assert check(fa, lse=None) == S["FA_ERR_NULL"]
     assert check(fa, q=A + 8) == S["FA_ERR_ALIGN"]

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import attn_inputs
-from parity_util import announce, assert_parity, default_scale, gpu_errors, to_gpu
+from parity_util import announce, assert_parity, default_scale, gpu_errors, record, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -44,8 +44,7 @@ def test_workload_parity_br128(fa, w):
     o, lse = run_br(fa, q, k, v, w.scale, 128)
     rows = None if w.full_rows else attn_inputs.rows_for(w)
     err = gpu_errors(q, k, v, o, lse, w.scale, rows=rows)
-    print(f"  br=128 {w.name}: max|dO|={err['max_dO']:.3e} max|dLSE|={err['max_dLSE']:.3e} "
-          f"E_unf={err['E_unf']:.3e}")
+    record("fused", w.name, err, br=128)
     assert_parity(err, f"br=128 {w.name}")
 
 

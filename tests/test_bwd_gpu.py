@@ -13,7 +13,7 @@ import torch
 
 import attn_inputs
 from oracle import attention_backward_fp64, attention_backward_unfused_bf16, attention_fp64
-from parity_util import announce, to_gpu
+from parity_util import announce, record, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -78,7 +78,8 @@ def test_bwd_parity(fa, B, H, N, d, seed, sigma):
     q, k, v, dO = make_case(B, H, N, d, seed, sigma)
     grads = run_bwd(fa, q, k, v, dO, scale)
     err, unf = bwd_errors(q, k, v, dO, grads, scale)
-    print("  " + "  ".join(f"{n}: {err[n]:.3e} (2x unfused {2 * unf[n]:.3e})" for n in NAMES))
+    record("backward", f"b{B}h{H}_n{N}_d{d}_s{sigma}", {f"max_d{n}": err[n] for n in NAMES} |
+           {f"E_unf_{n}": unf[n] for n in NAMES})
     for n in NAMES:
         assert err[n] <= 2.0 * unf[n] + 1e-6, (n, err[n], unf[n])
 
@@ -104,7 +105,20 @@ def test_bwd_parity_full_size_sampled_heads(fa):
     q, k, v, dO = make_case(w.B, w.H, w.N, w.d, w.seed)
     grads = run_bwd(fa, q, k, v, dO, w.scale)
     err, unf = bwd_errors(q, k, v, dO, grads, w.scale, heads=[(0, 0), (0, 31)])
-    print("  " + "  ".join(f"{n}: {err[n]:.3e} (2x unfused {2 * unf[n]:.3e})" for n in NAMES))
+    record("backward", f"{w.name}_heads_0_31", {f"max_d{n}": err[n] for n in NAMES} |
+           {f"E_unf_{n}": unf[n] for n in NAMES})
+    for n in NAMES:
+        assert err[n] <= 2.0 * unf[n] + 1e-6, (n, err[n], unf[n])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_negative_scale(fa, d):
+    """A negative scale: the gradients of the softmax of the negated scores."""
+    announce(f"bwd negative scale d={d}")
+    scale = -1.0 / np.sqrt(d)
+    q, k, v, dO = make_case(1, 2, 333, d, 400 + d, 2.0)
+    grads = run_bwd(fa, q, k, v, dO, scale)
+    err, unf = bwd_errors(q, k, v, dO, grads, scale)
     for n in NAMES:
         assert err[n] <= 2.0 * unf[n] + 1e-6, (n, err[n], unf[n])
 

@@ -11,7 +11,7 @@ import torch
 
 import attn_inputs
 from attn_inputs import DecodeWorkload
-from parity_util import announce, assert_parity, decode_errors, to_gpu
+from parity_util import announce, assert_parity, decode_errors, record, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -55,9 +55,22 @@ def test_decode_parity(fa, w):
     if w.check_heads:
         heads = attn_inputs.sample_heads(w.B, w.H, w.check_heads, seed=2000 + w.seed)
     err = decode_errors(q, k, v, o, lse, w.scale, heads=heads)
-    print(f"  {w.name}: max|dO|={err['max_dO']:.3e} beyond rounding={err['max_dO_beyond_rounding']:.3e} "
-          f"max|dLSE|={err['max_dLSE']:.3e} E_unf={err['E_unf']:.3e}")
+    record("decode", w.name, err, splits=splits, chunk=chunk)
     assert_parity(err, w.name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Nq,Nk", [(1, 777), (4, 3000), (16, 5000)])
+def test_decode_negative_scale(fa, d, Nq, Nk):
+    """A negative scale: the softmax of the negated scores, against the oracle."""
+    w = DecodeWorkload(f"neg_q{Nq}_k{Nk}_d{d}", 1, 2, Nq, Nk, d, seed=130 + Nq)
+    announce(f"decode negative scale {w.name}")
+    q, k, v = attn_inputs.make_decode_workload(w)
+    qg, kg, vg = to_gpu(q, k, v)
+    scale = -1.0 / math.sqrt(d)
+    o, lse = fa.decode_forward(qg, kg, vg, scale=scale)
+    torch.cuda.synchronize()
+    assert_parity(decode_errors(q, k, v, o, lse, scale), w.name)
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -291,21 +291,6 @@ def test_brute_force_against_closed_forms():
 # The bf16 unfused yardstick
 # ---------------------------------------------------------------------------
 
-def test_unfused_bf16_error_bound():
-    """Its deviation from the fp64 result is within the rounding it introduces:
-    bf16 P (relative 2^-9 per weight) and bf16 O (relative 2^-9), plus fp32 noise."""
-    q, k, v = attn_inputs.make_qkv(1, 2, 300, 64, seed=37)
-    scale = 0.125
-    O64, L64 = attention_fp64(attn_inputs.bf16_to_f64(q), attn_inputs.bf16_to_f64(k),
-                              attn_inputs.bf16_to_f64(v), scale)
-    Ou, Lu = attention_unfused_bf16(q, k, v, scale)
-    vmax = float(v.abs().max())
-    bound = 2.0 ** -9 * vmax + 2.0 ** -9 * np.abs(O64) + 1e-5
-    assert (np.abs(Ou - O64) <= bound).all()
-    assert np.abs(Ou - O64).max() > 0  # the 16-bit P does introduce error
-    np.testing.assert_allclose(Lu, L64, atol=1e-4)
-
-
 def test_unfused_bf16_exact_case():
     """Uniform scores with N a power of two: P = 1/N exactly in bf16, and V rows
     that are small integers make every step exact, so O equals the mean exactly."""
@@ -317,6 +302,90 @@ def test_unfused_bf16_exact_case():
     np.testing.assert_array_equal(Ou, torch.tensor(attn_inputs.bf16_to_f64(v)).mean(dim=2, keepdim=True)
                                   .to(torch.bfloat16).double().numpy().repeat(N, axis=2))
     np.testing.assert_allclose(Lu, math.log(N), atol=1e-6)
+
+
+YARDSTICK = os.path.join(os.path.dirname(__file__), "golden", "yardstick_cases.json")
+
+
+def check_yardstick_golden(impl):
+    """The hand-derived cases of tests/golden/yardstick_cases.json: inputs on which
+    every fp32 step is exact, so the bf16 rounding of P (IO page, section 6) and
+    of O each decide the expected bits."""
+    with open(YARDSTICK) as f:
+        cases = json.load(f)["forward"]
+    for c in cases:
+        q, k, v = (torch.tensor(c[n], dtype=torch.float32).to(torch.bfloat16)[None, None] for n in "qkv")
+        assert all(torch.equal(t.float(), torch.tensor(c[n], dtype=torch.float32)[None, None])
+                   for t, n in zip((q, k, v), "qkv")), "inputs must be bf16 values"
+        O, L = impl(q, k, v, c["scale"])
+        np.testing.assert_array_equal(O[0, 0], np.array(c["O"]), err_msg=c["name"])
+        np.testing.assert_allclose(L[0, 0], np.array(c["LSE"]), rtol=0, atol=1e-6, err_msg=c["name"])
+
+
+def check_yardstick_error_bound(impl):
+    """Random inputs: the deviation from the fp64 result is within the rounding the
+    yardstick introduces (bf16 P, relative 2^-9 per weight; bf16 O, relative 2^-9),
+    and nonzero (the 16-bit P does introduce error)."""
+    q, k, v = attn_inputs.make_qkv(1, 2, 300, 64, seed=37)
+    scale = 0.125
+    O64, L64 = attention_fp64(attn_inputs.bf16_to_f64(q), attn_inputs.bf16_to_f64(k),
+                              attn_inputs.bf16_to_f64(v), scale)
+    Ou, Lu = impl(q, k, v, scale)
+    vmax = float(v.abs().max())
+    bound = 2.0 ** -9 * vmax + 2.0 ** -9 * np.abs(O64) + 1e-5
+    assert (np.abs(Ou - O64) <= bound).all()
+    assert np.abs(Ou - O64).max() > 0
+    np.testing.assert_allclose(Lu, L64, atol=1e-4)
+
+
+YARDSTICK_PINS = [check_yardstick_golden, check_yardstick_error_bound]
+
+
+def test_unfused_bf16_yardstick_pins():
+    for pin in YARDSTICK_PINS:
+        pin(attention_unfused_bf16)
+
+
+def _round_bf16_toward_zero(t):
+    """fp32 -> bf16 by dropping the low 16 bits (truncation, not nearest-even)."""
+    return (t.contiguous().view(torch.int32) & -65536).view(torch.float32)
+
+
+def _mut_unfused(kind):
+    """Copies of the yardstick with one plausible mistake at a rounding point."""
+    def impl(q, k, v, scale, rows=None):
+        B, H, N, d = q.shape
+        O = np.empty((B, H, N, d))
+        L = np.empty((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                S = (q[b, h].float() @ k[b, h].float().T) * torch.tensor(scale, dtype=torch.float32)
+                m = S.max(dim=1).values
+                E = torch.exp(S - m[:, None])
+                l = E.sum(dim=1)
+                P = E / l[:, None]
+                if kind == "p_fp16":
+                    P = P.to(torch.float16).float()
+                elif kind == "p_truncated":
+                    P = _round_bf16_toward_zero(P)
+                elif kind != "p_fp32":
+                    P = P.to(torch.bfloat16).float()
+                o = P @ v[b, h].float()
+                O[b, h] = (o if kind == "o_fp32" else o.to(torch.bfloat16)).double().numpy()
+                L[b, h] = (m + torch.log(l)).double().numpy()
+        return O, L
+    return impl
+
+
+@pytest.mark.parametrize("kind", ["p_fp32", "o_fp32", "p_fp16", "p_truncated"])
+def test_yardstick_planted_mistakes_are_caught(kind):
+    failed = []
+    for pin in YARDSTICK_PINS:
+        try:
+            pin(_mut_unfused(kind))
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"yardstick mistake {kind} passed every pin"
 
 
 # ---------------------------------------------------------------------------

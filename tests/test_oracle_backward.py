@@ -6,7 +6,9 @@ own fp64 softmax, closed forms (scale = 0, dO = 0), and the invariants the
 softmax Jacobian implies (the rows of dS sum to zero, so the key gradients sum to
 zero; the rows of P sum to one, so the value gradients sum to the upstream rows).
 Planted mistakes in copies of the oracle must each fail a pin."""
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -141,9 +143,29 @@ def test_backward_planted_mistakes_are_caught(kind):
     assert failed, f"planted mistake {kind} passed every pin"
 
 
-def test_backward_unfused_bf16_is_close():
-    """The bf16 yardstick stays within bf16-level relative error of the oracle, and
-    does differ from it (the 16-bit P and dS introduce error)."""
+YARDSTICK = os.path.join(os.path.dirname(__file__), "golden", "yardstick_cases.json")
+
+
+def check_yardstick_golden(impl):
+    """The hand-derived backward cases of tests/golden/yardstick_cases.json: every
+    fp32 step is exact there, so the bf16 rounding of P, of dS and of the three
+    outputs each decide the expected bits, and dP or D rounded to bf16 would
+    change them."""
+    with open(YARDSTICK) as f:
+        cases = json.load(f)["backward"]
+    for c in cases:
+        ins = [torch.tensor(c[n], dtype=torch.float32).to(torch.bfloat16)[None, None]
+               for n in ("q", "k", "v", "o", "dO")]
+        for t, n in zip(ins, ("q", "k", "v", "o", "dO")):
+            assert torch.equal(t.float()[0, 0], torch.tensor(c[n], dtype=torch.float32)), "inputs must be bf16"
+        got = impl(*ins, c["scale"])
+        for g, n in zip(got, ("dQ", "dK", "dV")):
+            np.testing.assert_array_equal(g[0, 0], np.array(c[n]), err_msg=f"{c['name']} {n}")
+
+
+def check_yardstick_close(impl):
+    """Random inputs: within bf16-level relative error of the fp64 oracle, and not
+    equal to it (the 16-bit P and dS introduce error)."""
     q, k, v = attn_inputs.make_qkv(1, 2, 200, 64, seed=61)
     g = torch.Generator().manual_seed(62)
     dO = torch.randn(q.shape, generator=g).to(torch.bfloat16)
@@ -151,8 +173,57 @@ def test_backward_unfused_bf16_is_close():
     f = attn_inputs.bf16_to_f64
     o = torch.tensor(attention_fp64(f(q), f(k), f(v), scale)[0]).to(torch.bfloat16)
     ref = attention_backward_fp64(f(q), f(k), f(v), f(dO), scale)
-    emu = attention_backward_unfused_bf16(q, k, v, o, dO, scale)
+    emu = impl(q, k, v, o, dO, scale)
     for r, e in zip(ref, emu):
         scale_r = np.abs(r).max()
         err = np.abs(e - r).max()
         assert 0 < err <= 0.02 * scale_r, (err, scale_r)
+
+
+YARDSTICK_PINS = [check_yardstick_golden, check_yardstick_close]
+
+
+def test_backward_unfused_bf16_pins():
+    for pin in YARDSTICK_PINS:
+        pin(attention_backward_unfused_bf16)
+
+
+def _yardstick_mutant(kind):
+    """Copies of the backward yardstick with one plausible mistake at a rounding point."""
+    def impl(q, k, v, o, dO, scale):
+        out = [np.empty(tuple(t.shape)) for t in (q, k, v)]
+        sc = torch.tensor(scale, dtype=torch.float32)
+        rnd = (lambda t: t) if kind == "outputs_fp32" else (lambda t: t.to(torch.bfloat16))
+        for b in range(q.shape[0]):
+            for h in range(q.shape[1]):
+                Q, K, V, O, G = (t[b, h].float() for t in (q, k, v, o, dO))
+                S = (Q @ K.T) * sc
+                E = torch.exp(S - S.max(dim=1, keepdim=True).values)
+                P = E / E.sum(dim=1, keepdim=True)
+                if kind != "p_fp32":
+                    P = P.to(torch.bfloat16).float()
+                dV = rnd(P.T @ G)
+                dP = G @ V.T
+                if kind == "dp_bf16":
+                    dP = dP.to(torch.bfloat16).float()
+                D = (G * O).sum(dim=1, keepdim=True)
+                dS = P * (dP - D)
+                if kind != "ds_fp32":
+                    dS = dS.to(torch.bfloat16).float()
+                dQ = rnd((dS @ K) * sc)
+                dK = rnd((dS.T @ Q) * sc)
+                for arr, t in zip(out, (dQ, dK, dV)):
+                    arr[b, h] = t.double().numpy()
+        return tuple(out)
+    return impl
+
+
+@pytest.mark.parametrize("kind", ["p_fp32", "ds_fp32", "dp_bf16", "outputs_fp32"])
+def test_backward_yardstick_planted_mistakes_are_caught(kind):
+    failed = []
+    for pin in YARDSTICK_PINS:
+        try:
+            pin(_yardstick_mutant(kind))
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"yardstick mistake {kind} passed every pin"
