@@ -361,10 +361,10 @@ def decode_cpu_baseline(w, q, k, v, target_s: float = 10.0):
 
 
 def graph_chunks(steps: int) -> int:
-    """Number of equal graph replays the `steps` timed launches are split into: up to
-    five, each of at least two launches, so the timing has a spread."""
+    """Number of equal graph replays the `steps` timed launches are split into (up to
+    five, the largest that divides `steps`), so that the timing has a spread."""
     for r in (5, 4, 3, 2):
-        if steps % r == 0 and steps // r >= 2:
+        if steps % r == 0:
             return r
     return 1
 
@@ -372,10 +372,12 @@ def graph_chunks(steps: int) -> int:
 def time_launches(torch, launch, steps, stream, use_graph):
     """Run exactly `steps` timed launches of `launch(stream)` and return (per-launch ms
     list, wall seconds). With use_graph, steps/R launches are captured once in a HIP
-    graph (launched on torch's capture stream; R = graph_chunks(steps)), replayed once
-    untimed, then replayed R times, each replay between two events on `stream`: the
-    list holds each replay's time over its launch count. Otherwise each launch is
-    issued eagerly between its own pair of events."""
+    graph (launched on torch's capture stream; R = graph_chunks(steps)) and replayed
+    R times untimed (the first replay also uploads the graph; together they run the
+    same `steps` launches untimed as a single graph of all of them would), then R
+    times more, each replay between two events on `stream`: the list holds each
+    replay's time over its launch count. Otherwise each launch is issued eagerly
+    between its own pair of events."""
     if use_graph:
         r = graph_chunks(steps)
         per = steps // r
@@ -383,7 +385,8 @@ def time_launches(torch, launch, steps, stream, use_graph):
         with torch.cuda.graph(g):
             for _ in range(per):
                 launch(None)  # torch's current stream is the capture stream here
-        g.replay()
+        for _ in range(r):
+            g.replay()
         torch.cuda.synchronize()
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(r)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(r)]

@@ -26,7 +26,7 @@ HASH_PATH = LIB_PATH + ".srchash"  # sha256 of the sources and flags libfa.so wa
 
 def source_hash() -> str:
     """sha256 over the compile flags and the bytes of every source and header."""
-    h = hashlib.sha256(" ".join(compile_command("libfa.so")[1:]).encode())
+    h = hashlib.sha256(" ".join(FLAGS).encode())
     for path in [os.path.join(CSRC, s) for s in SOURCES] + HEADERS:
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
@@ -50,15 +50,17 @@ def hipcc() -> str:
     return path
 
 
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed fp32 VALU ops are kept out of generated code on this part
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
 def compile_command(out: str) -> list[str]:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    return [
-        shutil.which("hipcc") or "/opt/rocm/bin/hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 VALU ops are kept out of generated code on this part
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
-        *srcs, "-o", out,
-    ]
+    return [hipcc(), *FLAGS, *srcs, "-o", out]
 
 
 def build_library(verbose: bool = False) -> str:
