@@ -56,7 +56,8 @@ typedef enum {
   FA_ERR_OVERFLOW = -7,  /* sizes overflow 64-bit byte counts or the launch grid */
   FA_ERR_WORKSPACE = -8, /* workspace missing, too small, misaligned or overlapping */
   FA_ERR_HIP = -9,       /* the HIP runtime reported an error */
-  FA_ERR_DEVICE = -10    /* the current device is not gfx950 */
+  FA_ERR_DEVICE = -10,   /* the current device is not gfx950 */
+  FA_ERR_SCRATCH = -11   /* the problem needs more than the library's fixed scratch buffer */
 } fa_status;
 
 /*
@@ -175,6 +176,27 @@ int fa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* l
  * FA_ERR_OVERFLOW (then *workspace_bytes is 0). Pure host code.
  */
 int fa_decode_plan(int B, int H, int Nq, int Nk, int d, int* splits, int* chunk, size_t* workspace_bytes);
+
+/*
+ * fa_decode_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * kernels, split and results as fa_decode_fwd (bit for bit), but the partial
+ * results of the key split go to a fixed device array of FA_DECODE_SCRATCH_BYTES
+ * inside the library instead of a caller workspace; the array exists once per GPU
+ * and is held until the process ends. The call allocates nothing, frees nothing
+ * and issues no memset (the split writes every partial it reads back). The first
+ * call on a device looks the array's address up for that device.
+ *
+ * Every call on one GPU shares that GPU's array: calls ordered on one stream are
+ * safe, but calls that can overlap in time on one GPU (other streams or threads
+ * without ordering between them) race on it and give wrong results. Returns
+ * FA_ERR_SCRATCH, before any HIP call, when the shape needs more than
+ * FA_DECODE_SCRATCH_BYTES (the workspace_bytes of fa_decode_plan); otherwise as
+ * fa_decode_fwd.
+ */
+#define FA_DECODE_SCRATCH_BYTES (32u << 20)
+int fa_decode_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Nq, int Nk, int d, float scale, void* stream);
 
 /* Argument validation of fa_decode_fwd, without a GPU. Pure host code. */
 int fa_decode_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse,

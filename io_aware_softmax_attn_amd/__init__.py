@@ -21,19 +21,21 @@ __all__ = [
     "FaError", "lib", "fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks",
     "fa_check_args", "fa_status_string", "fa_version", "forward", "unfused_forward",
     "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args", "decode_forward", "DECODE_MAX_NQ",
+    "fa_decode_fwd_noalloc", "DECODE_SCRATCH_BYTES",
     "fa_fwd_tile_order", "TILE_ORDERS", "fa_fwd_blocks", "fa_bwd", "fa_bwd_workspace_bytes", "backward",
     "STATUS",
 ]
 
 DECODE_MAX_NQ = 16  # FA_DECODE_MAX_NQ
+DECODE_SCRATCH_BYTES = 32 << 20  # FA_DECODE_SCRATCH_BYTES
 TILE_ORDERS = {"xcd": 0, "dispatch": 1, "qtile_major": 2}  # orders of fa_fwd_tile_order
 
 STATUS = {
     "FA_OK": 0, "FA_ERR_NULL": -1, "FA_ERR_SHAPE": -2, "FA_ERR_HEADDIM": -3, "FA_ERR_ALIGN": -4,
     "FA_ERR_SCALE": -5, "FA_ERR_ALIAS": -6, "FA_ERR_OVERFLOW": -7, "FA_ERR_WORKSPACE": -8,
-    "FA_ERR_HIP": -9, "FA_ERR_DEVICE": -10,
+    "FA_ERR_HIP": -9, "FA_ERR_DEVICE": -10, "FA_ERR_SCRATCH": -11,
 }
-_ARG_ERRORS = {-1, -2, -3, -4, -5, -6, -7, -8}
+_ARG_ERRORS = {-1, -2, -3, -4, -5, -6, -7, -8, -11}
 
 
 class FaError(RuntimeError):
@@ -74,6 +76,8 @@ def _load() -> ctypes.CDLL:
     dll.fa_fwd_blocks.restype = i
     dll.fa_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp]
     dll.fa_decode_fwd.restype = i
+    dll.fa_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    dll.fa_decode_fwd_noalloc.restype = i
     dll.fa_decode_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(sz)]
     dll.fa_decode_plan.restype = i
     dll.fa_decode_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz]
@@ -273,6 +277,19 @@ def fa_decode_fwd(q, k, v, o, lse, workspace, scale=None, stream=None):
     with torch.cuda.device(q.device):
         _raise(lib.fa_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                                  _ptr(workspace), nbytes, _stream_handle(stream, q.device)), "fa_decode_fwd")
+    return o, lse
+
+
+def fa_decode_fwd_noalloc(q, k, v, o, lse, scale=None, stream=None):
+    """fa_decode_fwd into caller-provided ``o`` and ``lse`` without a workspace: the
+    library's fixed per-GPU scratch array (DECODE_SCRATCH_BYTES) holds the partial
+    results. Calls that can overlap in time on one GPU race on that array."""
+    B, H, Nq, Nk, d = _decode_shape_of(q, k, v, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(q.device):
+        _raise(lib.fa_decode_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                                         float(scale), _stream_handle(stream, q.device)), "fa_decode_fwd_noalloc")
     return o, lse
 
 

@@ -44,6 +44,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "workspace is missing, too small, misaligned or overlaps a tensor";
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+    case FA_ERR_SCRATCH: return "the problem needs more than FA_DECODE_SCRATCH_BYTES of the library's fixed scratch buffer";
     default: return "unknown status";
   }
 }
@@ -127,8 +128,17 @@ int fa_decode_plan(int B, int H, int Nq, int Nk, int d, int* splits, int* chunk,
   return FA_OK;
 }
 
-int fa_decode_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
-                         int Nq, int Nk, int d, float scale, const void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Every check of fa_decode_check_args except the workspace's: shapes, pointers,
+// alignment and overlaps. *need receives the workspace bytes (0 for an empty
+// problem).
+int decode_check_tensors(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
+                         int Nq, int Nk, int d, float scale, size_t* need_out, size_t* qs_out, size_t* ks_out,
+                         size_t* ls_out) {
+  *need_out = 0;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
@@ -156,11 +166,43 @@ int fa_decode_check_args(const void* q, const void* k, const void* v, const void
   if (overlaps(o, qs, q, qs) || overlaps(o, qs, k, ks) || overlaps(o, qs, v, ks) || overlaps(lse, ls, q, qs) ||
       overlaps(lse, ls, k, ks) || overlaps(lse, ls, v, ks) || overlaps(lse, ls, o, qs))
     return FA_ERR_ALIAS;
+  *need_out = need;
+  *qs_out = qs;
+  *ks_out = ks;
+  *ls_out = ls;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
+                         int Nq, int Nk, int d, float scale, const void* workspace, size_t workspace_bytes) {
+  size_t need = 0, qs = 0, ks = 0, ls = 0;
+  const int st = decode_check_tensors(q, k, v, o, lse, B, H, Nq, Nk, d, scale, &need, &qs, &ks, &ls);
+  if (st != FA_OK || need == 0) return st;
+  auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
   if (!workspace || workspace_bytes < need || misaligned(workspace, 16)) return FA_ERR_WORKSPACE;
   if (overlaps(workspace, need, q, qs) || overlaps(workspace, need, k, ks) || overlaps(workspace, need, v, ks) ||
       overlaps(workspace, need, o, qs) || overlaps(workspace, need, lse, ls))
     return FA_ERR_WORKSPACE;
   return FA_OK;
+}
+
+int fa_decode_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                          int Nk, int d, float scale, void* stream) {
+  size_t need = 0, qs = 0, ks = 0, ls = 0;
+  const int st = decode_check_tensors(q, k, v, o, lse, B, H, Nq, Nk, d, scale, &need, &qs, &ks, &ls);
+  if (st != FA_OK || need == 0) return st;  // need == 0: empty problem, a no-op
+  if (need > (size_t)FA_DECODE_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  const int dev = fa::device_is_gfx950();
+  if (dev < 0) return dev;
+  if (dev == 0) return FA_ERR_DEVICE;
+  void* buf = nullptr;  // device address of the fixed scratch array on this device
+  const int sst = fa::decode_scratch(&buf);
+  if (sst != FA_OK) return sst;
+  return fa::launch_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, buf, stream);
 }
 
 int fa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,

@@ -18,12 +18,21 @@
 // batches of keys; the waves' states are merged through LDS at the end.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_internal.h"
 
 namespace fa {
+
+// The partial results of fa_decode_fwd_noalloc: a fixed array in device memory, one
+// per GPU, held until the process ends. In host code `scratch` names a host-side
+// stand-in, not the device array: host code only ever uses the address that
+// decode_scratch() looks up for the current device.
+static __device__ __attribute__((used)) __align__(256) unsigned char scratch[FA_DECODE_SCRATCH_BYTES];
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -313,6 +322,30 @@ void launch_split_d(const void* q, const void* k, const void* v, float* po, floa
 }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+int decode_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_DEVICE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // Once per device, with that device current: its copy of the array has its own address.
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return FA_OK;
+}
 
 int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
                   int d, float scale, void* workspace, void* stream) {

@@ -38,6 +38,10 @@ DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d);
 int launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
                   int d, float scale, void* workspace, void* stream);
 
+// Device address, on the current device, of the decode path's fixed scratch array
+// (FA_DECODE_SCRATCH_BYTES), looked up once per device; returns a fa_status code.
+int decode_scratch(void** ptr);
+
 // Enqueue the three backward kernels; returns a fa_status code. Arguments already
 // validated; workspace holds at least fa_bwd_workspace_bytes(B, H, N).
 int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,

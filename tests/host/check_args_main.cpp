@@ -49,6 +49,13 @@ int launch_bwd(const void*, const void*, const void*, const void*, const float*,
   return FA_OK;
 }
 int device_is_gfx950() { return g_device; }
+int g_scratch_lookups = 0;
+int decode_scratch(void** ptr) {
+  ++g_scratch_lookups;
+  static unsigned char stand_in[256];
+  *ptr = stand_in;
+  return FA_OK;
+}
 }  // namespace fa
 
 int main() {
@@ -218,6 +225,22 @@ int main() {
   }
   EXPECT(std::strcmp(fa_status_string(12345), "unknown status") == 0);
   EXPECT(fa_version() >= 10000);
+
+  // The allocation-free decode: argument errors and a shape whose partial results do
+  // not fit the fixed scratch array return before any launch or scratch lookup.
+  {
+    const int before_nl = g_launches;
+    EXPECT(fa_decode_fwd_noalloc(q, k, v, o, lse, B, H, 17, N, d, sc, nullptr) == FA_ERR_SHAPE);
+    EXPECT(fa_decode_fwd_noalloc(q, k, v, q, lse, B, H, 4, N, d, sc, nullptr) == FA_ERR_ALIAS);
+    EXPECT(fa_decode_fwd_noalloc(nullptr, nullptr, nullptr, nullptr, nullptr, 0, H, 4, N, d, sc, nullptr) == FA_OK);
+    // 64*64 heads of 16 rows, one key chunk each: 16.9 M floats of partials > 32 MiB
+    EXPECT(fa_decode_fwd_noalloc(q, k, v, o, lse, 64, 64, 16, 4096, 128, sc, nullptr) == FA_ERR_SCRATCH ||
+           fa_decode_fwd_noalloc(q, k, v, o, lse, 64, 64, 16, 4096, 128, sc, nullptr) == FA_ERR_ALIAS);
+    EXPECT(g_launches == before_nl && fa::g_scratch_lookups == 0);
+    // a valid small call looks the array up and launches once
+    EXPECT(fa_decode_fwd_noalloc(q, k, v, o, lse, B, H, 4, N, d, sc, nullptr) == FA_OK);
+    EXPECT(g_launches == before_nl + 1 && fa::g_scratch_lookups == 1);
+  }
 
   std::free(ws);
   std::free(q);

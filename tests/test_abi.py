@@ -28,7 +28,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_unfused_fwd", "fa_unfused_workspace_bytes", "fa_select_blocks", "fa_check_args",
               "fa_status_string", "fa_version", "fa_decode_fwd", "fa_decode_plan", "fa_decode_check_args",
-              "fa_fwd_tile_order", "fa_bwd", "fa_bwd_workspace_bytes"):
+              "fa_fwd_tile_order", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_fwd_noalloc"):
         assert n in names
 
 
@@ -235,6 +235,33 @@ def test_decode_fwd_rejects_before_any_hip_call(fa):
     assert lib.fa_decode_fwd(A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 1, 32, 100, 128, 0.1, 16 * A, 1 << 20,
                              None) == S["FA_ERR_SHAPE"]
     assert lib.fa_decode_fwd(None, None, None, None, None, 1, 1, 0, 100, 128, 0.1, None, 0, None) == 0
+
+
+def test_decode_noalloc_rejects_before_any_hip_call(fa):
+    """The allocation-free decode checks its arguments, then that the shape's partial
+    results fit the fixed scratch array, before any HIP call (the pointers here are
+    fake)."""
+    S = fa.STATUS
+    lib = fa.lib
+    big = 1 << 36  # fake tensors far apart
+
+    def call(B, H, Nq, Nk, d=128, q=A, scale=0.1):
+        return lib.fa_decode_fwd_noalloc(q, 2 * big, 3 * big, 4 * big, 5 * big, B, H, Nq, Nk, d, scale, None)
+
+    assert call(1, 1, 32, 100) == S["FA_ERR_SHAPE"]
+    assert call(1, 1, 4, 100, d=96) == S["FA_ERR_HEADDIM"]
+    assert call(1, 1, 4, 100, q=None) == S["FA_ERR_NULL"]
+    assert call(1, 1, 4, 100, scale=float("inf")) == S["FA_ERR_SCALE"]
+    assert call(0, 1, 4, 100, q=None) == 0  # empty problem: a no-op
+    # one key chunk per head (the grid fills the chip with heads): the partials of
+    # B*H*Nq rows take (d + 1) * 4 bytes each, which passes the fixed size here
+    B, H, Nq, Nk, d = 64, 64, 16, 4096, 128
+    splits, _, need = fa.fa_decode_plan(B, H, Nq, Nk, d)
+    assert splits == 1 and need == (B * H * Nq * (d + 1) * 4 + 255) // 256 * 256 > fa.DECODE_SCRATCH_BYTES
+    assert call(B, H, Nq, Nk, d) == S["FA_ERR_SCRATCH"]
+    assert "FA_DECODE_SCRATCH_BYTES" in fa.fa_status_string(S["FA_ERR_SCRATCH"])
+    with pytest.raises(ValueError):
+        fa._raise(S["FA_ERR_SCRATCH"], "fa_decode_fwd_noalloc")
 
 
 def test_tile_order_rejects_before_any_hip_call(fa):
