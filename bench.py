@@ -255,6 +255,55 @@ def summarize_io_sweep(sweep_dir, copy_bytes):
     print("\n".join(lines))
 
 
+def summarize_parity(jsonl, command, out_md="profiles/parity_gpu.md"):
+    """No GPU work: turn the raw error records the GPU parity tests append to
+    FA_PARITY_RECORD (one JSON object per case) into a table, and copy the records
+    next to it (profiles/parity_gpu.jsonl)."""
+    recs = [json.loads(line) for line in open(jsonl) if line.strip()]
+    out_md = os.path.join(ROOT, out_md)
+    with open(os.path.splitext(out_md)[0] + ".jsonl", "w") as f:
+        for r in recs:
+            f.write(json.dumps(r) + "\n")
+
+    def g(x, fmt="{:.3e}"):
+        return "-" if x is None else fmt.format(x)
+
+    lines = [
+        "# GPU parity against the fp64 oracle (raw figures)",
+        "",
+        f"Command: `{command}`",
+        "",
+        "Gates: max|dO| <= 1e-2 on every element with |O| < 2; from |O| = 2 on, max(|dO| - half bf16 ulp) "
+        "<= 1e-2 (the output rounding alone is up to 0.0078 there); max|dLSE| <= 1e-3; max|dO| <= 2 x E_unf, "
+        "the error of the bf16 unfused computation on the same rows. `n > 1e-2` counts elements whose raw "
+        "|dO| exceeds 1e-2.",
+        "",
+        "## Forward (fused, both query-tile heights), unfused baseline, decode",
+        "",
+        "| path | case | BR | rows | max\|O_ref\| | max\|dO\| | max\|dO\| (\|O\|<2) | beyond half-ulp (\|O\|>=2) "
+        "| n > 1e-2 / elements | max\|dLSE\| | E_unf | max\|dO\| / E_unf |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for r in recs:
+        if r["kind"] == "backward":
+            continue
+        ratio = r["max_dO"] / r["E_unf"] if r.get("E_unf") else None
+        lines.append(f"| {r['kind']} | {r['case']} | {r.get('br', '-')} | {r['rows_checked']} | "
+                     f"{r['max_abs_O_ref']:.3f} | {g(r['max_dO'])} | {g(r['max_dO_narrow'])} | "
+                     f"{g(r['max_dO_wide_beyond_rounding'])} | {r['n_over_tol']} / {r['n_elements']} | "
+                     f"{g(r['max_dLSE'])} | {g(r.get('E_unf'))} | {g(ratio, '{:.2f}')} |")
+    bw = [r for r in recs if r["kind"] == "backward"]
+    if bw:
+        lines += ["", "## Backward (gate: each gradient's max error <= 2 x the bf16 unfused backward's)", "",
+                  "| case | dQ | 2 E_unf(dQ) | dK | 2 E_unf(dK) | dV | 2 E_unf(dV) |", "|---|---|---|---|---|---|---|"]
+        for r in bw:
+            lines.append(f"| {r['case']} | " + " | ".join(
+                f"{g(r['max_d' + n])} | {g(2 * r['E_unf_' + n])}" for n in ("dQ", "dK", "dV")) + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out_md)
+
+
 def summarize_trace(stats_csv, command, workload, steps=50):
     """Write the per-kernel duration summary of a rocprofv3 --stats run, with the
     command that produced it and the algorithmic rate at the average duration."""
@@ -666,6 +715,9 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="no GPU work: turn a rocprofv3 --kernel-trace --stats kernel_stats.csv into "
                          "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin")
+    ap.add_argument("--summarize-parity", nargs=2, metavar=("JSONL", "COMMAND"),
+                    help="no GPU work: turn the FA_PARITY_RECORD file of a GPU test run into "
+                         "profiles/parity_gpu.md (+ .jsonl), recording COMMAND as its origin")
     ap.add_argument("--tile-order", type=int, default=0, choices=(0, 1, 2),
                     help="fused path only: workgroup-to-tile order of fa_fwd_tile_order (0 = fa_fwd's)")
     ap.add_argument("--eager", action="store_true",
@@ -698,6 +750,9 @@ def main():
         return
     if args.summarize_io_sweep:
         summarize_io_sweep(args.summarize_io_sweep, args.copy_calibration)
+        return
+    if args.summarize_parity:
+        summarize_parity(*args.summarize_parity)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload, args.steps)
