@@ -476,7 +476,11 @@ def decode_bench(args):
     import attn_inputs
     import io_aware_softmax_attn_amd as fa
 
-    w = attn_inputs.DECODE_HEADLINE if args.workload is None else attn_inputs.DECODE_BY_NAME[args.workload]
+    if args.shape:
+        B, H, Nq, Nk, d = (int(x) for x in args.shape.split(","))
+        w = attn_inputs.DecodeWorkload(f"dec_b{B}h{H}_q{Nq}_k{Nk}_d{d}", B, H, Nq, Nk, d, seed=0)
+    else:
+        w = attn_inputs.DECODE_HEADLINE if args.workload is None else attn_inputs.DECODE_BY_NAME[args.workload]
     q, k, v = attn_inputs.make_decode_workload(w)
     dev = torch.device("cuda:0")
     qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
@@ -548,7 +552,11 @@ def backward_bench(args):
     import attn_inputs
     import io_aware_softmax_attn_amd as fa
 
-    w = attn_inputs.HEADLINE if args.workload is None else attn_inputs.WORKLOAD_BY_NAME[args.workload]
+    if args.shape:
+        B, H, N, d = (int(x) for x in args.shape.split(","))
+        w = attn_inputs.Workload(f"b{B}h{H}_n{N}_d{d}", B, H, N, d, seed=0)
+    else:
+        w = attn_inputs.HEADLINE if args.workload is None else attn_inputs.WORKLOAD_BY_NAME[args.workload]
     q, k, v = attn_inputs.make_workload(w)
     g = torch.Generator().manual_seed(w.seed + 7919)
     dO = torch.randn(q.shape, generator=g).to(torch.bfloat16)
@@ -728,7 +736,8 @@ def main():
     ap.add_argument("--br", type=int, default=0, choices=(0, 128, 256),
                     help="fused path only: query rows per workgroup (fa_fwd_blocks); 0 = the selector's choice")
     ap.add_argument("--shape", metavar="B,H,N,d",
-                    help="a fused-path shape outside the named workloads (seed 0, unit Gaussian inputs)")
+                    help="a shape outside the named workloads (seed 0, unit Gaussian inputs): B,H,N,d for the "
+                         "forward or the backward, B,H,Nq,Nk,d with --decode")
     ap.add_argument("--summarize-io-sweep", metavar="DIR",
                     help="no GPU work: turn the FETCH_SIZE/WRITE_SIZE runs of the tile-order sweep under DIR "
                          "into profiles/fa_fwd_io_sweep.md (with --copy-calibration BYTES)")

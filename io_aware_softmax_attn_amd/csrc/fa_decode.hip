@@ -272,6 +272,244 @@ __global__ void __launch_bounds__(256) dec_split_kernel(const __bf16* __restrict
   }
 }
 
+// Kernel 1 for 5 to 16 query rows, on the matrix cores. With more query rows the
+// VALU kernel above runs out of vector issue slots before HBM runs out of bytes
+// (four dot2, four DPP adds, an exp2 and eight FMAs per key and query). Here the
+// query rows are padded to 16 and both products run as v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T   (16 keys x 16 queries per product, 32 of d per k-step);
+//   O^T += V^T P^T (16 of d x 16 queries per product, 32 keys per k-step).
+// Each wave streams its own 32-key tiles of the chunk (tiles w, w+4, ...). K rows
+// are loaded straight into the A operands (lane l: key l%16, d 8*(l/16)..+8 of a
+// k-step); V rows are loaded coalesced, written to the wave's own LDS tile and read
+// back transposed with ds_read_b64_tr_b16. A lane holds scores of keys 4G+i and
+// 16+4G+i (G = l/16) for query l%16; the V^T operand reads use the same key order,
+// so the contraction pairs each P with its V row. The online softmax is the FA1
+// page's update per 32-key tile (steps 1-5) with the exact running max. P enters
+// the PV product as two bf16 terms, P = hi + lo with lo = bf16(P - hi), so the sum
+// keeps about 16 significant bits of P, like the fp32 P of the VALU kernel; the
+// matrix cores have the slots to spare, as this path is bound by HBM.
+template <int D>
+struct MfmaDecCfg {
+  static constexpr int kTileKeys = 32;                      // keys per wave per step
+  static constexpr int kKS = D / 32;                        // k-steps of S^T = K Q^T
+  static constexpr int kDB = D / 16;                        // 16-row d-blocks of O^T
+  static constexpr int kChunks = D / 8;                     // 16-byte chunks per K/V row
+  static constexpr int kRowsPerLoad = 64 / kChunks;         // rows one wave-wide 16-byte load covers
+  static constexpr int kVLoads = kTileKeys / kRowsPerLoad;  // V row loads per lane per tile
+  static constexpr int kTileBytes = kTileKeys * 2 * D;      // one wave's V tile in LDS
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#define FA_LDS_AS __attribute__((address_space(3)))
+
+// XOR swizzle of the 16-byte chunk index of V tile row r (a key). A transposing read
+// by 16 lanes covers 4 consecutive rows x 2 adjacent chunks (an even chunk and the
+// next); the even XOR values 2*(r%4) send the 4 rows to 8 distinct chunks, so the
+// 16 lanes hit 8 distinct 16-byte bank groups. At D = 128 bit 2 of the row also
+// selects the other half of the row, separating neighbouring lane groups.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  int x = 2 * (r & 3);
+  if constexpr (D == 128) x |= 8 * ((r >> 2) & 1);
+  return x;
+}
+
+// Max and sum over the four lanes l%16 + 16*G (G = 0..3) that hold one query.
+__device__ __forceinline__ float qmax4(float x) {
+  f32x2_t r = swap16(x);
+  x = fmaxf(r[0], r[1]);
+  r = swap32(x);
+  return fmaxf(r[0], r[1]);
+}
+__device__ __forceinline__ float qsum4(float x) {
+  f32x2_t r = swap16(x);
+  x = r[0] + r[1];
+  r = swap32(x);
+  return r[0] + r[1];
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) dec_split_mfma_kernel(const __bf16* __restrict__ q,
+                                                                const __bf16* __restrict__ k,
+                                                                const __bf16* __restrict__ v,
+                                                                float* __restrict__ part_o,
+                                                                float* __restrict__ part_lse, int Nq, int Nk,
+                                                                int chunk, int S, float c) {
+  using C = MfmaDecCfg<D>;
+  constexpr int KS = C::kKS, DB = C::kDB, VL = C::kVLoads;
+  // The waves' V tiles during the loop; the waves' partial O^T ([4][16][D] fp32, the
+  // same 256*D bytes) for the merge after it.
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * C::kTileBytes];
+  __shared__ float sm[4][16], sl[4][16];
+  static_assert(4 * C::kTileBytes == 4 * 16 * D * 4, "partial O^T must fit the V tiles");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = lane >> 4, j = lane & 15;
+  const int s = blockIdx.x % S;
+  const size_t bh = blockIdx.x / S;
+  const int k0 = s * chunk;
+  const int k1 = min(k0 + chunk, Nk);
+  const int ntiles = (k1 - k0 + C::kTileKeys - 1) / C::kTileKeys;
+
+  // Q^T operands: lane l holds query l%16 (zero past Nq), d 32*ks + 8*(l/16) .. +8.
+  bf16x8_t qB[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qB[ks] = bf16x8_t{};
+    if (j < Nq) qB[ks] = *(const bf16x8_t*)(q + (bh * Nq + j) * D + 32 * ks + 8 * G);
+  }
+  const __bf16* kh = k + bh * (size_t)Nk * D;
+  const __bf16* vh = v + bh * (size_t)Nk * D;
+  const unsigned stage = (unsigned)(uintptr_t)(FA_LDS_AS unsigned char*)smem + (unsigned)(wave * C::kTileBytes);
+  // This lane's LDS byte offsets: its V row writes, and its transposing reads of
+  // d-block db, k-slot half r (keys 16r + 4G + 0..3, column 16db + j).
+  unsigned vw[VL], vr[DB][2];
+#pragma unroll
+  for (int u = 0; u < VL; ++u) {
+    const int row = u * C::kRowsPerLoad + lane / C::kChunks, ch = lane % C::kChunks;
+    vw[u] = stage + (unsigned)(row * 2 * D + ((ch ^ vswz<D>(row)) << 4));
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 16 * r + 4 * G + (j >> 2), dcol = 16 * db + 4 * (j & 3);
+      vr[db][r] = stage + (unsigned)(row * 2 * D + (((dcol >> 3) ^ vswz<D>(row)) << 4) + 2 * (dcol & 7));
+    }
+  }
+
+  float m = -__builtin_inff(), lsum = 0.0f;
+  f32x4_t acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4_t{};
+
+  // Tile t of the chunk: keys k0 + 32t ..; rows past Nk read row Nk-1 (inside the
+  // head) and are masked.
+  auto load = [&](int t, u32x4_t (&kr)[2][KS], u32x4_t (&vrow)[VL]) {
+    const int key0 = k0 + t * C::kTileKeys;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const size_t key = (size_t)min(key0 + 16 * b + j, Nk - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kr[b][ks] = __builtin_nontemporal_load((const u32x4_t*)(kh + key * D + 32 * ks + 8 * G));
+    }
+#pragma unroll
+    for (int u = 0; u < VL; ++u) {
+      const size_t row = (size_t)min(key0 + u * C::kRowsPerLoad + lane / C::kChunks, Nk - 1);
+      vrow[u] = __builtin_nontemporal_load((const u32x4_t*)(vh + row * D + 8 * (lane % C::kChunks)));
+    }
+  };
+  auto process = [&](int t, const u32x4_t (&kr)[2][KS], const u32x4_t (&vrow)[VL]) {
+    // V rows into this wave's tile (the wave's own LDS accesses run in order, so the
+    // transposing reads below see them, and the previous tile's reads are done).
+#pragma unroll
+    for (int u = 0; u < VL; ++u) *(FA_LDS_AS u32x4_t*)(uintptr_t)vw[u] = vrow[u];
+    f32x4_t sc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      sc[b] = f32x4_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[b][ks]), qB[ks], sc[b], 0, 0,
+                                                        0);
+    }
+    const int key0 = k0 + t * C::kTileKeys;
+    float tv[2][4];
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool live = key0 + 16 * b + 4 * G + i < k1;
+        tv[b][i] = live ? sc[b][i] * c : -__builtin_inff();
+        mt = fmaxf(mt, tv[b][i]);
+      }
+    }
+    // Steps 1-2: the tile's row max (every tile holds a live key, so it is finite),
+    // the new running max and the factor for the old state.
+    const float mn = fmaxf(m, qmax4(mt));
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    bf16x8_t phi, plo;
+    float ps = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(tv[b][i] - mn);
+        ps += p;
+        const __bf16 hi = (__bf16)p;
+        phi[4 * b + i] = hi;
+        plo[4 * b + i] = (__bf16)(p - (float)hi);
+      }
+    }
+    lsum = __builtin_fmaf(lsum, alpha, ps);
+    // Steps 3-5: rescale the accumulator and add P V for this tile.
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] *= alpha;
+      const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS_AS i16x4_t*)(uintptr_t)vr[db][0]);
+      const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS_AS i16x4_t*)(uintptr_t)vr[db][1]);
+      const bf16x8_t va = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo4), __builtin_bit_cast(bf16x4_t, hi4),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[db], 0, 0, 0);
+    }
+  };
+
+  // The next tile's rows are loaded before the current one is processed.
+  u32x4_t kc[2][KS], vc[VL], kn[2][KS], vn[VL];
+  if (wave < ntiles) load(wave, kc, vc);
+  for (int t = wave; t < ntiles; t += 4) {
+    const bool more = t + 4 < ntiles;
+    if (more) load(t + 4, kn, vn);
+    process(t, kc, vc);
+    if (more) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kc[b][ks] = kn[b][ks];
+      }
+#pragma unroll
+      for (int u = 0; u < VL; ++u) vc[u] = vn[u];
+    }
+  }
+
+  // A lane's sum covers its own keys; the query's sum adds the four lanes holding it.
+  lsum = qsum4(lsum);
+  __syncthreads();  // every wave is done with its V tile: the LDS now holds partial O^T
+  float* so = (float*)smem;
+  if (G == 0) {
+    sm[wave][j] = m;
+    sl[wave][j] = lsum;
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) so[(wave * 16 + j) * D + 16 * db + 4 * G + i] = acc[db][i];
+  }
+  __syncthreads();
+  const size_t out_row0 = (bh * S + s) * (size_t)Nq;
+  for (int e = threadIdx.x; e < Nq * D; e += 256) {
+    const int i = e / D, col = e % D;
+    float mx = sm[0][i];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, sm[w][i]);
+    float den = 0.0f, num = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = __builtin_amdgcn_exp2f(sm[w][i] - mx);  // 0 for a wave that saw no key
+      den = __builtin_fmaf(a, sl[w][i], den);
+      num = __builtin_fmaf(a, so[(w * 16 + i) * D + col], num);
+    }
+    part_o[(out_row0 + i) * D + col] = num / den;
+    if (col == 0) part_lse[out_row0 + i] = mx + __builtin_log2f(den);
+  }
+}
+
 // Kernel 2: one wave per query row (b, h, i); lane l owns columns D/64*l .. +D/64-1.
 template <int D>
 __global__ void __launch_bounds__(256) dec_merge_kernel(const float* __restrict__ part_o,
@@ -317,8 +555,9 @@ void launch_split_d(const void* q, const void* k, const void* v, float* po, floa
   if (Nq <= 1) launch_split<D, 1>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
   else if (Nq <= 2) launch_split<D, 2>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
   else if (Nq <= 4) launch_split<D, 4>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
-  else if (Nq <= 8) launch_split<D, 8>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
-  else launch_split<D, 16>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
+  else
+    hipLaunchKernelGGL((dec_split_mfma_kernel<D>), dim3((unsigned)(BH * p.splits)), dim3(256), 0, st,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, po, pl, Nq, Nk, p.chunk, p.splits, c);
 }
 
 }  // namespace
