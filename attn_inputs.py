@@ -116,6 +116,7 @@ DECODE_WORKLOADS = (
     DecodeWorkload("dec_b1h32_q1_k131072_d128", 1, 32, 1, 131072, 128, seed=101, check_heads=6),
     DecodeWorkload("dec_b4h16_q4_k4096_d64", 4, 16, 4, 4096, 64, seed=102),
     DecodeWorkload("dec_b2h8_q16_k30001_d128_wide", 2, 8, 16, 30001, 128, seed=103, sigma_qk=2.5),
+    DecodeWorkload("dec_b16h32_q16_k8192_d128", 16, 32, 16, 8192, 128, seed=104, check_heads=24),
 )
 DECODE_BY_NAME = {w.name: w for w in DECODE_WORKLOADS}
 DECODE_HEADLINE = DECODE_WORKLOADS[0]

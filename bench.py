@@ -115,7 +115,7 @@ def _read_counter_csv(path):
 UNFUSED_KERNELS = ("unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel")
 
 
-DECODE_KERNELS = ("dec_split_kernel", "dec_merge_kernel")
+DECODE_KERNELS = ("dec_split_kernel", "dec_split_mfma_kernel", "dec_merge_kernel")
 BWD_KERNELS = ("bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
 BWD_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_bwd.hip")
 
@@ -143,6 +143,8 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, dec
         """Average KiB per launch: one kernel (fused) or the sum of the three."""
         names = (DECODE_KERNELS if decode else BWD_KERNELS if backward else UNFUSED_KERNELS if unfused
                  else ("fa_fwd_kernel",))
+        # the decode split runs one of two kernels, by the number of query rows
+        names = [n for n in names if any(n in k for (k, c) in table if c == counter)]
         total, raw = 0.0, []
         for name in names:
             vals = pick(table, counter, lambda k, n=name: n in k)
@@ -176,6 +178,10 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, unfused=False, dec
         "write_scale": round(w_scale, 4),
         "fetch_kib_raw_per_launch": fa_fetch,
         "write_kib_raw_per_launch": fa_write,
+        "commands": [f"rocprofv3 --pmc {ctr} -d <out>/pmc_{w.name}_{ctr} -o c --output-format csv -- python3 bench.py "
+                     + ("--decode " if decode else "--backward " if backward else "--unfused " if unfused else "")
+                     + f"--workload {w.name} --launches-only --steps 2 --warmup 1 --copy-calibration {copy_bytes}"
+                     for ctr in ("FETCH_SIZE", "WRITE_SIZE")],
     }
     stem = "fa_decode" if decode else "fa_bwd" if backward else "fa_unfused" if unfused else "fa_fwd"
     if backward:  # algorithmic bytes: read q, k, v, o, dO and lse, write dq, dk, dv
@@ -304,9 +310,11 @@ def summarize_parity(jsonl, command, out_md="profiles/parity_gpu.md"):
     print(out_md)
 
 
-def summarize_trace(stats_csv, command, workload, steps=50):
+def summarize_trace(stats_csv, command, workload, steps=50, bench_json=None):
     """Write the per-kernel duration summary of a rocprofv3 --stats run, with the
-    command that produced it and the algorithmic rate at the average duration."""
+    command that produced it and the algorithmic rate at the average duration. With
+    bench_json (the JSON line of a bench.py run made in the same GPU session), quote
+    that line's rate and step time next to the trace."""
     import csv
 
     import attn_inputs
@@ -314,7 +322,7 @@ def summarize_trace(stats_csv, command, workload, steps=50):
     rows = list(csv.DictReader(open(stats_csv)))
     backward = any("bwd_dq_kernel" in r["Name"] for r in rows)
     fused = not backward and any("fa_fwd_kernel" in r["Name"] for r in rows)
-    decode = any("dec_split_kernel" in r["Name"] for r in rows)
+    decode = any("dec_split" in r["Name"] for r in rows)
     if decode:
         w = attn_inputs.DECODE_HEADLINE if workload is None else attn_inputs.DECODE_BY_NAME[workload]
         shape = f"B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d}"
@@ -375,8 +383,66 @@ def summarize_trace(stats_csv, command, workload, steps=50):
                       f"{MFMA_BF16_PEAK_TFLOPS} TFLOP/s bf16 MFMA peak. The forward launch in the table makes O and "
                       f"LSE for the backward's inputs.",
                   f"Kernel source sha256[:16] of fa_bwd.hip: {kernel_source_hash(BWD_SRC)}."]
+    if bench_json:
+        rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        r = rec["roofline"]
+        cmd = f"python3 bench.py --gpus {rec['n_gpus']} --steps {rec['steps']} --warmup {rec['warmup']}"
+        lines += ["", f"`{cmd}`, run just before the trace in the same GPU session: {rec['value']} {rec['unit']} "
+                      f"({r['frac']} of peak), ms_per_step {rec['ms_per_step']}; per launch {r['kernel_ms_avg']} ms "
+                      f"on average over the {rec['steps']} timed launches (median {r.get('kernel_ms_median')}, "
+                      f"min {r.get('kernel_ms_min')}, max {r.get('kernel_ms_max')} over {r.get('timing_samples')} "
+                      f"samples, each {r.get('timing_sample')})."]
     stem = "fa_fwd" if fused else "fa_decode" if decode else "fa_bwd" if backward else "fa_unfused"
     path = os.path.join(ROOT, "profiles", f"{stem}_{w.name}_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+SQ_COUNTERS = ("SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_INSTS_LDS")
+
+
+def summarize_counters(counter_csv, command, workload):
+    """Matrix-core occupancy and instruction mix of each kernel in a rocprofv3 --pmc
+    run of SQ_COUNTERS, averaged over its dispatches after the first.
+    SQ_BUSY_CYCLES sums over the 32 shader engines and SQ_VALU_MFMA_BUSY_CYCLES over
+    the 1024 SIMDs, so busy = MFMA / (BUSY / 32 * 1024)."""
+    import collections
+    import csv
+
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(counter_csv)):
+        key = int(r["Dispatch_Id"])
+        per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[key] = r["Kernel_Name"]
+    kernels = collections.defaultdict(list)
+    for key in sorted(per):
+        base = re.sub(r"\(.*", "", names[key])
+        kernels[base].append(per[key])
+    lines = [f"# SQ counters, workload {workload}", "", "Command, run from the repository root with TMPDIR=/tmp:", "",
+             "```", command, "```", "",
+             "| kernel | dispatches | MFMA busy | VALU insts / MFMA insts | LDS insts / MFMA insts | "
+             "VALU-MFMA co-issue / MFMA busy | waves waiting on a dependency | kernel cycles |",
+             "|---|---|---|---|---|---|---|---|"]
+    for base, ds in kernels.items():
+        if not any(x in base for x in ("fa_fwd_kernel", "dec_", "bwd_", "unf_")):
+            continue
+        use = ds[1:] if len(ds) > 1 else ds
+        c = {n: sum(d.get(n, 0.0) for d in use) / len(use) for n in SQ_COUNTERS}
+        busy = c["SQ_BUSY_CYCLES"] / 32.0
+        mf = c["SQ_VALU_MFMA_BUSY_CYCLES"]
+        m = re.search(r"\d+([a-z_]+_kernel)((?:ILi\d+E)*(?:Li\d+E)*)", base)
+        short = (m.group(1) + "<" + ",".join(re.findall(r"Li(\d+)E", m.group(2))) + ">") if m else base[:60]
+        lines.append(f"| `{short}` | {len(use)} | {mf / (busy * 1024):.3f} | "
+                     f"{c['SQ_INSTS_VALU'] / max(c['SQ_INSTS_MFMA'], 1):.2f} | "
+                     f"{c['SQ_INSTS_LDS'] / max(c['SQ_INSTS_MFMA'], 1):.2f} | "
+                     f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / max(mf, 1):.2f} | "
+                     f"{c['SQ_WAIT_INST_ANY'] / max(c['SQ_WAVE_CYCLES'], 1):.2f} | {busy:.4g} |")
+    stem = "fa_fwd" if any("fa_fwd_kernel" in b for b in kernels) else "fa_decode" if any(
+        "dec_" in b for b in kernels) else "fa_bwd"
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_counters.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -720,9 +786,13 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: read two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-calibration run and write profiles/fa_fwd_<workload>_traffic.json")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"),
+    ap.add_argument("--summarize-trace", nargs="+", metavar="STATS_CSV COMMAND [BENCH_JSON]",
                     help="no GPU work: turn a rocprofv3 --kernel-trace --stats kernel_stats.csv into "
-                         "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin")
+                         "profiles/<kernel>_<workload>_kernel_trace.md, recording COMMAND as its origin, and "
+                         "quoting the bench.py JSON line of the same GPU session when given")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_CSV", "COMMAND"),
+                    help="no GPU work: turn a rocprofv3 --pmc counter_collection.csv of SQ counters into "
+                         "profiles/<kernel>_<workload>_counters.md")
     ap.add_argument("--summarize-parity", nargs=2, metavar=("JSONL", "COMMAND"),
                     help="no GPU work: turn the FA_PARITY_RECORD file of a GPU test run into "
                          "profiles/parity_gpu.md (+ .jsonl), recording COMMAND as its origin")
@@ -764,7 +834,11 @@ def main():
         summarize_parity(*args.summarize_parity)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload, args.steps)
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload, args.steps,
+                        args.summarize_trace[2] if len(args.summarize_trace) > 2 else None)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
