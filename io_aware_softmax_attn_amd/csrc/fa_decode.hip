@@ -3,8 +3,10 @@
 // with prefill (sections 常见误区 and 自测题: decode is bound by memory traffic,
 // not by arithmetic). Per key the work is 4*Nq*d flops against 4*d bytes of K and
 // V, at most 16 flops per byte, far below the matrix cores' ridge, so this path is
-// written for HBM bandwidth: coalesced 16-byte row loads, dot products and the
-// PV sum on the vector ALUs in fp32, and enough independent workgroups in flight.
+// written for HBM bandwidth: coalesced 16-byte row loads and enough independent
+// workgroups in flight. One query row runs its dot products and PV sum on the
+// vector ALUs in fp32; 2 to 16 rows run them on the matrix cores (the vector issue
+// slots run out first there).
 //
 // The key range of each (b, h) is split into chunks, one workgroup per chunk
 // (kernel 1), whose partial results are merged afterwards (kernel 2):
@@ -272,10 +274,11 @@ __global__ void __launch_bounds__(256) dec_split_kernel(const __bf16* __restrict
   }
 }
 
-// Kernel 1 for 5 to 16 query rows, on the matrix cores. With more query rows the
+// Kernel 1 for 2 to 16 query rows, on the matrix cores. With more query rows the
 // VALU kernel above runs out of vector issue slots before HBM runs out of bytes
-// (four dot2, four DPP adds, an exp2 and eight FMAs per key and query). Here the
-// query rows are padded to 16 and both products run as v_mfma_f32_16x16x32_bf16:
+// (four dot2, four DPP adds, an exp2 and eight FMAs per key and query: 4.4 TB/s at
+// 8 rows, 2.0 at 16); this kernel streams at the same rate for every row count, and
+// from 2 rows on at least as fast as the VALU kernel. Here the query rows are padded to 16 and both products run as v_mfma_f32_16x16x32_bf16:
 //   S^T = K Q^T   (16 keys x 16 queries per product, 32 of d per k-step);
 //   O^T += V^T P^T (16 of d x 16 queries per product, 32 keys per k-step).
 // Each wave streams its own 32-key tiles of the chunk (tiles w, w+4, ...). K rows
@@ -553,8 +556,6 @@ template <int D>
 void launch_split_d(const void* q, const void* k, const void* v, float* po, float* pl, int BH, int Nq, int Nk,
                     const DecodePlan& p, float c, hipStream_t st) {
   if (Nq <= 1) launch_split<D, 1>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
-  else if (Nq <= 2) launch_split<D, 2>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
-  else if (Nq <= 4) launch_split<D, 4>(q, k, v, po, pl, BH, Nq, Nk, p, c, st);
   else
     hipLaunchKernelGGL((dec_split_mfma_kernel<D>), dim3((unsigned)(BH * p.splits)), dim3(256), 0, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, po, pl, Nq, Nk, p.chunk, p.splits, c);

@@ -73,15 +73,15 @@ Blocks select_blocks(int d, int N, int B, int H) {
 // Each (b, h) is cut into S chunks of `chunk` keys, one workgroup per chunk. The
 // split kernel streams K and V, so the grid aims at one full round of resident
 // workgroups: 256 CUs times the workgroups one CU holds at once, which the kernel's
-// register use sets: the vector kernel for up to 1, 2 and 4 query rows takes 70, 80
-// and 110 VGPRs (7, 6 and 4 workgroups of 4 waves); the matrix-core kernel for 5 to
-// 16 rows takes 219 VGPRs at d = 128 and 118 at d = 64 (2 and 4 workgroups). A
+// register use sets: the vector kernel for one query row takes 70 VGPRs (7
+// workgroups of 4 waves); the matrix-core kernel for 2 to 16 rows takes 219 VGPRs at
+// d = 128 and 118 at d = 64 (2 and 4 workgroups). A
 // second, partial round would leave most CUs idle at the end; more, shorter chunks
 // add partial results to write and merge. Chunks hold at least 256 keys and are
 // multiples of 128 keys, a whole number of the kernel's key batches for both head
 // dimensions. Depends on the shape only, not on the device.
 namespace {
-int resident_per_cu(int Nq, int d) { return Nq <= 1 ? 7 : Nq <= 2 ? 6 : Nq <= 4 ? 4 : d == 64 ? 4 : 2; }
+int resident_per_cu(int Nq, int d) { return Nq <= 1 ? 7 : d == 64 ? 4 : 2; }
 }  // namespace
 
 DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d) {

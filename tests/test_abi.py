@@ -172,12 +172,11 @@ def test_decode_plan_covers_every_key(fa, B, H, Nq, Nk, d):
 
 
 def test_decode_plan_fills_the_chip(fa):
-    # About one round of resident workgroups (256 CUs x 7, 6, 4 per CU for up to 1,
-    # 2, 4 query rows; the matrix-core kernel for 5-16 rows: 2 per CU at d = 128, 4
-    # at d = 64) when the keys allow it; no chunk below 256 keys unless the whole
-    # sequence is shorter.
-    resident = {(1, 128): 7, (2, 128): 6, (3, 128): 4, (4, 64): 4, (5, 128): 2, (8, 128): 2, (16, 128): 2,
-                (8, 64): 4, (16, 64): 4}
+    # About one round of resident workgroups (256 CUs x 7 per CU for one query row;
+    # the matrix-core kernel for 2-16 rows: 2 per CU at d = 128, 4 at d = 64) when
+    # the keys allow it; no chunk below 256 keys unless the whole sequence is shorter.
+    resident = {(1, 128): 7, (1, 64): 7, (2, 128): 2, (3, 128): 2, (4, 64): 4, (5, 128): 2, (8, 128): 2,
+                (16, 128): 2, (8, 64): 4, (16, 64): 4}
     for B, H, Nk in ((16, 32, 8192), (1, 32, 131072), (1, 1, 1 << 20), (4, 16, 4096), (2, 8, 30001)):
         for (nq, d), per_cu in resident.items():
             splits, chunk, _ = fa.fa_decode_plan(B, H, nq, Nk, d)
