@@ -440,8 +440,9 @@ def summarize_counters(counter_csv, command, workload):
                      f"{c['SQ_INSTS_LDS'] / max(c['SQ_INSTS_MFMA'], 1):.2f} | "
                      f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / max(mf, 1):.2f} | "
                      f"{c['SQ_WAIT_INST_ANY'] / max(c['SQ_WAVE_CYCLES'], 1):.2f} | {busy:.4g} |")
-    stem = "fa_fwd" if any("fa_fwd_kernel" in b for b in kernels) else "fa_decode" if any(
-        "dec_" in b for b in kernels) else "fa_bwd"
+    # a backward run also launches the forward that makes its O and LSE
+    stem = "fa_bwd" if any("bwd_" in b for b in kernels) else "fa_decode" if any(
+        "dec_" in b for b in kernels) else "fa_fwd"
     path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_counters.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
