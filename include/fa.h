@@ -157,10 +157,12 @@ int fa_check_args(const void* q, const void* k, const void* v, const void* o, co
  * Two kernels: the first splits each head's keys into chunks, one workgroup per
  * chunk, and writes each chunk's normalised partial O and its LSE (fp32) to the
  * workspace; the second merges the partials of each row with the FA1 page's
- * update (derivation steps 2 and 4-5) applied to whole chunks. Scores and
- * probabilities stay in fp32 (bf16 products accumulate exactly in fp32); O is
- * rounded to bf16 (nearest-even) once, at the end. When B*H*Nq == 0 the call is
- * a no-op. Deterministic for a given shape: the split depends on the shape only.
+ * update (derivation steps 2 and 4-5) applied to whole chunks. Scores are fp32
+ * (bf16 products accumulate exactly in fp32); probabilities keep about 16 bits
+ * (fp32 for one query row; as a bf16 pair, value and remainder, on the matrix
+ * cores for 2 to 16 rows); O is rounded to bf16 (nearest-even) once, at the end.
+ * When B*H*Nq == 0 the call is a no-op. Deterministic for a given shape: the
+ * split depends on the shape only.
  */
 #define FA_DECODE_MAX_NQ 16
 #define FA_DECODE_MAX_NK (1 << 30)
@@ -227,7 +229,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  * rounded up to 256; 0 if negative or the product overflows size_t. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
-/* Static, NUL-terminated description of a status code. */
+/* Utilities. Static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);
 
 /* Library version, major*10000 + minor*100 + patch. */
