@@ -387,6 +387,8 @@ def summarize_trace(stats_csv, command, workload, steps=50, bench_json=None):
         rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
         r = rec["roofline"]
         cmd = f"python3 bench.py --gpus {rec['n_gpus']} --steps {rec['steps']} --warmup {rec['warmup']}"
+        if rec["config"].get("workload") != attn_inputs.HEADLINE.name:
+            cmd += f" --workload {rec['config']['workload']} --no-cpu-baseline"
         lines += ["", f"`{cmd}`, run just before the trace in the same GPU session: {rec['value']} {rec['unit']} "
                       f"({r['frac']} of peak), ms_per_step {rec['ms_per_step']}; per launch {r['kernel_ms_avg']} ms "
                       f"on average over the {rec['steps']} timed launches (median {r.get('kernel_ms_median')}, "

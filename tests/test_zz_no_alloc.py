@@ -62,3 +62,39 @@ def test_noalloc_decode_rejects_a_shape_beyond_the_array(fa):
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError, match="scratch"):
         fa.fa_decode_fwd_noalloc(q, k, k, o, lse)
+
+
+def test_noalloc_decode_graph_replays(fa):
+    """The allocation-free decode is meant for code under graph capture: capture one
+    call, then replay it with new inputs copied into the captured buffers, with an
+    eager call of another shape in between (which rewrites the scratch array), and
+    compare each replay with fa_decode_fwd on the same inputs, bit for bit."""
+    B, H, Nq, Nk, d = 4, 8, 6, 3000, 128
+    announce(f"graph fa_decode_fwd_noalloc B={B} H={H} Nq={Nq} Nk={Nk} d={d}")
+    q, k, v = to_gpu(*attn_inputs.make_decode_qkv(B, H, Nq, Nk, d, seed=150))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.fa_decode_fwd_noalloc(q, k, v, o, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fa_decode_fwd_noalloc(q, k, v, o, lse)
+    torch.cuda.synchronize()
+    oq, ok_, ov = to_gpu(*attn_inputs.make_decode_qkv(2, 3, 1, 5000, 64, seed=151))
+    for rep in range(3):
+        fresh = attn_inputs.make_decode_qkv(B, H, Nq, Nk, d, seed=160 + rep)
+        for dst, src in zip((q, k, v), fresh):
+            dst.copy_(src)
+        fa.decode_forward(oq, ok_, ov)  # another shape through the workspace entry point
+        fa.fa_decode_fwd_noalloc(oq, ok_, ov, torch.empty_like(oq),
+                                 torch.empty((2, 3, 1), dtype=torch.float32, device="cuda"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_ref, l_ref = fa.decode_forward(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"replay {rep}"
