@@ -48,6 +48,17 @@ def test_workload_parity_br128(fa, w):
     assert_parity(err, f"br=128 {w.name}")
 
 
+@pytest.mark.parametrize("N", [1, 33, 255, 257, 513, 1000, 2049])
+def test_ragged_lengths_br256_d64(fa, N):
+    """The 256-row kernel at d = 64, which the selector never picks (two co-resident
+    128-row workgroups win there), through fa_fwd_blocks."""
+    announce(f"br=256 d=64 ragged N={N}")
+    q, k, v = attn_inputs.make_qkv(2, 3, N, 64, seed=300 + N)
+    o, lse = run_br(fa, q, k, v, default_scale(64), 256)
+    err = gpu_errors(q, k, v, o, lse, default_scale(64))
+    assert_parity(err, f"br=256 N={N} d=64", check_yardstick=N > 1)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 31, 32, 33, 64, 65, 127, 128, 129, 255, 257, 383, 513])
 def test_ragged_lengths_br128(fa, d, N):

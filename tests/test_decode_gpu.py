@@ -60,6 +60,20 @@ def test_decode_parity(fa, w):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Nq", list(range(1, 17)))
+def test_decode_every_row_count(fa, d, Nq):
+    """Every row count the decode path takes (the vector kernel at one row, the
+    matrix-core kernel, rows padded to 16, from two on), with a key count that is no
+    multiple of a chunk or a 32-key tile and a few heads, against the oracle."""
+    Nk = 997 + 37 * Nq
+    w = DecodeWorkload(f"rows_q{Nq}_k{Nk}_d{d}", 2, 3, Nq, Nk, d, seed=200 + Nq + d)
+    announce(f"decode every row count {w.name}")
+    q, k, v = attn_inputs.make_decode_workload(w)
+    o, lse = run_decode(fa, w, q, k, v)
+    assert_parity(decode_errors(q, k, v, o, lse, w.scale), w.name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Nq,Nk", [(1, 777), (4, 3000), (16, 5000)])
 def test_decode_negative_scale(fa, d, Nq, Nk):
     """A negative scale: the softmax of the negated scores, against the oracle."""
