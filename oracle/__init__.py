@@ -19,8 +19,11 @@ backward.py holds the gradients of the forward (the chain rule through its three
 steps; the pages give no backward formulas, see its docstring).
 
 Every function is pinned by tests that do not re-type its formulas (closed forms,
-invariants, brute force, library special cases); no function here is "parity
-unpinned".
+invariants, brute force, library special cases); the two bf16 yardsticks
+(attention_unfused_bf16, attention_backward_unfused_bf16) also by hand-derived values
+on inputs whose every fp32 step is exact, so that each of their bf16 rounding points
+decides the expected bits (tests/golden/yardstick_cases.json). No function here is
+"parity unpinned".
 """
 from .backward import attention_backward_fp64, attention_backward_unfused_bf16  # noqa: F401
 from .attention import (  # noqa: F401
