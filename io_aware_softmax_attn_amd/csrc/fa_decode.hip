@@ -277,8 +277,9 @@ __global__ void __launch_bounds__(256) dec_split_kernel(const __bf16* __restrict
 // Kernel 1 for 2 to 16 query rows, on the matrix cores. With more query rows the
 // VALU kernel above runs out of vector issue slots before HBM runs out of bytes
 // (four dot2, four DPP adds, an exp2 and eight FMAs per key and query: 4.4 TB/s at
-// 8 rows, 2.0 at 16); this kernel streams at the same rate for every row count, and
-// from 2 rows on at least as fast as the VALU kernel. Here the query rows are padded to 16 and both products run as v_mfma_f32_16x16x32_bf16:
+// 8 rows, 2.0 at 16); this kernel streams at the same rate for every row count,
+// and from 2 rows on at least as fast as the VALU kernel. The query rows are padded
+// to 16 and both products run as v_mfma_f32_16x16x32_bf16:
 //   S^T = K Q^T   (16 keys x 16 queries per product, 32 of d per k-step);
 //   O^T += V^T P^T (16 of d x 16 queries per product, 32 keys per k-step).
 // Each wave streams its own 32-key tiles of the chunk (tiles w, w+4, ...). K rows
