@@ -384,7 +384,8 @@ def summarize_trace(stats_csv, command, workload, steps=50, bench_json=None):
                       f"LSE for the backward's inputs.",
                   f"Kernel source sha256[:16] of fa_bwd.hip: {kernel_source_hash(BWD_SRC)}."]
     if bench_json:
-        rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        with open(bench_json) as f:
+            rec = json.loads(f.read().strip().splitlines()[-1])
         r = rec["roofline"]
         cmd = f"python3 bench.py --gpus {rec['n_gpus']} --steps {rec['steps']} --warmup {rec['warmup']}"
         if rec["config"].get("workload") != attn_inputs.HEADLINE.name:

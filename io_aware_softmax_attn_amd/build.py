@@ -37,7 +37,10 @@ def check_built() -> None:
     """Raise unless libfa.so exists and was built from the current sources."""
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing")
-    recorded = open(HASH_PATH).read().strip() if os.path.exists(HASH_PATH) else None
+    recorded = None
+    if os.path.exists(HASH_PATH):
+        with open(HASH_PATH) as f:
+            recorded = f.read().strip()
     if recorded != source_hash():
         raise RuntimeError(f"{LIB_PATH} was built from other sources than the current ones; rebuild it with "
                            f"'python io_aware_softmax_attn_amd/build.py'")

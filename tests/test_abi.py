@@ -19,7 +19,8 @@ def fa():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
 
