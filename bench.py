@@ -10,6 +10,7 @@ in HBM before the timed region. Prints ONE JSON line.
   python bench.py --decode [--workload dec_...]   (decode-shaped forward, GB/s)
   python bench.py --backward [--workload NAME]    (backward dQ, dK, dV, TFLOP/s)
   python bench.py --all [--eager]      (one line per named forward workload)
+  python bench.py --gemm [--shape M,N,K]          (context: a bf16 hipBLASLt GEMM)
 
 The K timed launches of the fused forward are captured once in a HIP graph and
 replayed between two HIP events on the stream they run on; the average launch
@@ -707,6 +708,42 @@ def backward_bench(args):
 MEMORY_SHAPES = ((2, 16, 128, (1024, 2048, 4096, 8192)), (4, 16, 64, (1024, 2048, 4096, 8192)))
 
 
+def gemm_bench(args):
+    """Time a dense bf16 matrix product C = A B (torch.mm, which ROCm serves from
+    hipBLASLt), by default M = N = K = 8192: 2*8192^3 FLOP, the same count as one
+    forward launch at B=1 H=32 N=8192 d=128. Context only, not the product: the rate
+    a vendor-tuned contraction sustains on this part under the same power limit,
+    against the same 2.4 GHz peak. Timed like the forward (graph replays)."""
+    import torch
+
+    M, N, K = (int(x) for x in (args.shape or "8192,8192,8192").split(","))
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(0)
+    a = torch.randn((M, K), generator=g).to(torch.bfloat16).to(dev).contiguous()
+    b = torch.randn((K, N), generator=g).to(torch.bfloat16).to(dev).contiguous()
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch(s=stream):
+        torch.mm(a, b, out=c)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    use_graph = not (args.eager or args.launches_only)
+    per_ms, _ = time_launches(torch, launch, args.steps, stream, use_graph)
+    avg_ms = sum(per_ms) / len(per_ms)
+    flops = 2.0 * M * N * K
+    tflops = flops / (avg_ms * 1e-3) / 1e12
+    line = {"metric": f"bf16 GEMM TFLOP/s (context), M={M} N={N} K={K}", "value": round(tflops, 2),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"op": "torch.mm", "M": M, "N": N, "K": K, "launch": "graph" if use_graph else "eager"},
+            "frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "kernel_ms_avg": round(avg_ms, 4),
+            **timing_stats(per_ms, use_graph, args.steps)}
+    print(json.dumps(line), flush=True)
+
+
 def footprint_bytes(B: int, H: int, N: int, d: int, fused: bool) -> int:
     """Device bytes one forward holds at its peak: Q, K, V and O (bf16) and LSE
     (fp32), plus, on the unfused path, the score matrix S (fp32) and the
@@ -820,6 +857,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="the decode-shaped forward (few queries against many keys) instead of the prefill "
                          "benchmark; also selects the decode kernels for --summarize-pmc")
+    ap.add_argument("--gemm", action="store_true",
+                    help="context, not the product: time a bf16 torch.mm (hipBLASLt) of M,N,K (--shape, default "
+                         "8192,8192,8192, the forward benchmark's FLOP count) the same way")
     ap.add_argument("--memory", metavar="OUT_MD",
                     help="instead of timing: peak device memory of the fused and unfused forward over "
                          "a range of sequence lengths, written as a table to OUT_MD")
@@ -858,6 +898,9 @@ def main():
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ.setdefault(var, threads)
 
+    if args.gemm:
+        gemm_bench(args)
+        return
     if args.decode:
         decode_bench(args)
         return
