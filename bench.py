@@ -292,14 +292,14 @@ def summarize_parity(jsonl, command, out_md="profiles/parity_gpu.md"):
         "|---|---|---|---|---|---|---|---|---|---|---|---|",
     ]
     for r in recs:
-        if r["kind"] == "backward":
+        if r["kind"].startswith("backward"):
             continue
         ratio = r["max_dO"] / r["E_unf"] if r.get("E_unf") else None
         lines.append(f"| {r['kind']} | {r['case']} | {r.get('br', '-')} | {r['rows_checked']} | "
                      f"{r['max_abs_O_ref']:.3f} | {g(r['max_dO'])} | {g(r['max_dO_narrow'])} | "
                      f"{g(r['max_dO_wide_beyond_rounding'])} | {r['n_over_tol']} / {r['n_elements']} | "
                      f"{g(r['max_dLSE'])} | {g(r.get('E_unf'))} | {g(ratio, '{:.2f}')} |")
-    bw = [r for r in recs if r["kind"] == "backward"]
+    bw = [r for r in recs if r["kind"].startswith("backward")]
     if bw:
         lines += ["", "## Backward (gate: each gradient's max error <= 2 x the bf16 unfused backward's)", "",
                   "| case | dQ | 2 E_unf(dQ) | dK | 2 E_unf(dK) | dV | 2 E_unf(dV) |", "|---|---|---|---|---|---|---|"]
