@@ -47,3 +47,11 @@ def test_fused_line(eager):
 def test_backward_and_decode_lines(mode):
     rec = run_bench(mode, "--workload", "b1h1_n256_d64" if mode == "--backward" else "dec_b4h16_q4_k4096_d64")
     assert rec["config"]["launch"] == "graph" and rec["value"] > 0
+
+
+def test_gemm_context_line():
+    """The GEMM yardstick: one JSON line with the rate of a bf16 torch.mm of the given shape."""
+    rec = run_bench("--gemm", "--shape", "512,256,1024")
+    assert rec["config"] == {"op": "torch.mm", "M": 512, "N": 256, "K": 1024, "launch": "graph"}
+    assert rec["value"] > 0 and rec["timing_samples"] == 3
+    assert abs(rec["frac_of_peak"] - rec["value"] / 2516.6) < 1e-3
