@@ -306,6 +306,11 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
     constexpr bool kMasked = decltype(masked_tag)::value;
     constexpr unsigned KT = J * kStage, VT = KT + kTile;
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    // Two waves share each SIMD. A wave raises its issue priority while it issues
+    // its S and dP products (and a later tile's loads), so that the matrix core is
+    // fed by the wave in that phase while the other runs its softmax on the VALU
+    // (at B=1 H=32 N=8192 d=128: kernel cycles -11%, matrix cores 0.69 -> 0.78 busy).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s = mfma(rd_row(KT, ks), qf[ks], s);
@@ -314,6 +319,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
     // Issued after the S/dP reads, so those start right after the barrier (the
     // loads' asm is a compiler memory fence).
     issue(t + kStages - 1, lds + (unsigned)(((J + kStages - 1) % kStages) * kStage));
+    __builtin_amdgcn_s_setprio(0);
     float ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
