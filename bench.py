@@ -117,7 +117,7 @@ UNFUSED_KERNELS = ("unf_qk_kernel", "unf_softmax_kernel", "unf_pv_kernel")
 
 
 DECODE_KERNELS = ("dec_split_kernel", "dec_split_mfma_kernel", "dec_merge_kernel")
-BWD_KERNELS = ("bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
+BWD_KERNELS = ("bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_dkdv_pair_kernel")
 BWD_SRC = os.path.join(ROOT, "io_aware_softmax_attn_amd", "csrc", "fa_bwd.hip")
 
 

@@ -16,7 +16,9 @@
 //   bwd_dkdv  one workgroup per 128 keys, K and V held in registers: streams
 //             32-row Q/dO tiles through LDS, recomputes S = Q K^T and dP = dO V^T, and
 //             accumulates dV^T += dO^T P and dK^T += Q^T dS (each lane owns one key
-//             column; dO^T and Q^T come from LDS through transposing reads).
+//             column; dO^T and Q^T come from LDS through transposing reads). At
+//             d = 128 (bwd_dkdv_pair) the work of 32 keys is split over two waves
+//             that share a SIMD, one for S, P and dV, the other for dP, dS and dK.
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS enter
 // them as bf16 (nearest-even). The row order inside a 32-row block of the operand
 // read from LDS as rows is permuted (bits 2 and 3 swapped), which makes the
@@ -676,6 +678,272 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __
   }
 }
 
+// ---- kernel 3, d = 128: dK and dV with two waves per SIMD ----
+// Eight waves per workgroup of 128 keys, in pairs that share 32 keys. Waves 0-3
+// (the P role) hold K and the dV^T accumulator: per 32-row tile they compute
+// S = Q K^T and P = exp2(S c - LSE2), hand P (fp32) to their partner through LDS,
+// and accumulate dV^T += dO^T P. Waves 4-7 (the dS role) hold V and the dK^T
+// accumulator: they compute dP = dO V^T, take P from LDS, form dS = P o (dP - D)
+// and accumulate dK^T += Q^T dS. Each role runs 16 of a tile's 32 products, and a
+// SIMD holds one wave of each role (waves w and w + 4 of a workgroup share a SIMD),
+// so while one wave waits on its products or on LDS the other issues. The P role works one tile ahead: in step s it takes tile
+// s + 1 while its partner takes tile s, whose P it wrote in step s - 1. Every
+// product, the P and dS values and the accumulation order are those of the
+// one-wave kernel above, so the two give bitwise-equal gradients.
+template <int D>
+__global__ void __launch_bounds__(512, 1) bwd_dkdv_pair_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                             const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
+                                                             const float* __restrict__ dvec, const float* __restrict__ lse2,
+                                                             __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N,
+                                                             int tiles_per_head, int total_tiles, float c, float scale) {
+  constexpr int KS = D / 16, DB = D / 32, kTile = 32 * D * 2;
+  constexpr int kWaves = 8;
+  // Ring of Q/dO tiles of 32 rows: each stage holds the Q tile, the dO tile and a
+  // 1 KB vector area (LSE2 of the tile's rows at +0, D at +256; +512 takes the zero
+  // fills of the vector loads that waves 2-7 issue so that every wave issues the
+  // same number of loads per tile).
+  constexpr int kStages = 4, kVec = 1024;
+  constexpr int kStage = 2 * kTile + kVec;
+  constexpr int kChunks = D / 8;
+  constexpr int kLoads = kTile / 1024 / kWaves;  // 16-byte loads per wave per Q (or dO) tile
+  constexpr int kPerTile = 2 * kLoads + 1;       // this wave's loads per tile, vector load included
+  constexpr int kX = 32 * 32 * 4;                // one pair's P of one tile, fp32
+  static_assert(kLoads >= 1 && kTile % (1024 * kWaves) == 0, "tile loads must split evenly over the 8 waves");
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
+  __shared__ __attribute__((aligned(1024))) char xch[2 * 4 * kX];  // P hand-over, two tiles x four pairs
+  const unsigned lds = (unsigned)(uintptr_t)(LDS_AS char*)smem;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+  const int pair = wave & 3;
+  const bool role_p = wave < 4;
+  const int logical = remap_xcd(blockIdx.x, total_tiles);
+  const int bh = logical / tiles_per_head, kt0 = logical % tiles_per_head;
+  const size_t head = (size_t)bh * N * D;
+  const size_t rowvec = (size_t)bh * N;
+  const int krow = kt0 * 128 + pair * 32 + (lane & 31);
+
+  // K (P role) or V (dS role) of the pair's 32 keys: the B operand of S or dP.
+  const __bf16* kvsrc = role_p ? k : v;
+  bf16x8_t kv[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kv[ks] = bf16x8_t{};
+    if (krow < N) kv[ks] = *(const bf16x8_t*)(kvsrc + head + (size_t)krow * D + ks * 16 + g * 8);
+  }
+  // Consumed here, so the compiler waits for these loads once, in the prologue,
+  // rather than with a vmcnt(0) inside the loop, which would also wait for the
+  // tile loads in flight (the compiler does not count the asm loads).
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(kv[ks]));
+  f32x16_t acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+
+  const int T = (N + 31) / 32;
+  // Loads as in the one-wave kernel, over eight waves: lane l's 16 bytes of load i
+  // form slot p = (wave * kLoads + i) * 64 + l of the tile.
+  unsigned gofs[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int p = (wave * kLoads + i) * 64 + lane, row = p / kChunks;
+    gofs[i] = (unsigned)(row * D * 2 + (((p % kChunks) ^ swz<D>(row)) << 4));
+  }
+  const char* qh = (const char*)(q + head);
+  const char* dh = (const char*)(dO + head);
+  const float* vsrc = (wave == 0 ? lse2 : dvec) + rowvec;
+  const unsigned vdst = wave < 2 ? (unsigned)(2 * kTile + wave * 256) : (unsigned)(2 * kTile + 512);
+  auto issue = [&](int u, unsigned st) {
+    const u32x4_t rq = rows_rsrc(qh, u * 32, 32, N, D * 2);
+    const u32x4_t rd = rows_rsrc(dh, u * 32, 32, N, D * 2);
+    const unsigned dst = __builtin_amdgcn_readfirstlane(st + (unsigned)(wave * kLoads * 1024));
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) dma16(rq, gofs[i], dst + i * 1024);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) dma16(rd, gofs[i], dst + kTile + i * 1024);
+    const u32x4_t rv = rows_rsrc(vsrc, u * 32, 32, wave < 2 ? N : 0, 4);
+    dma4(rv, (unsigned)lane * 4u, __builtin_amdgcn_readfirstlane(st + vdst));
+  };
+  // Per-lane LDS addresses of the operand reads for a stage at offset 0, as in the
+  // one-wave kernel; the loop is unrolled over the four ring stages, so each stage
+  // offset rides in the ds_read immediate.
+  unsigned rofs[KS], tofs[DB][2];
+  {
+    const int rr = pi_row(lane & 31), trow = 8 * g + ((lane & 15) >> 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      rofs[ks] = lds + (unsigned)chunk_offset<D>(rr, 2 * ks + g);
+      asm volatile("" : "+v"(rofs[ks]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      tofs[db][0] = lds + (unsigned)(chunk_offset<D>(trow, col >> 3) + 2 * (col & 7));
+      tofs[db][1] = lds + (unsigned)(chunk_offset<D>(trow + 4, col >> 3) + 2 * (col & 7));
+      asm volatile("" : "+v"(tofs[db][0]), "+v"(tofs[db][1]));
+    }
+  }
+  static_assert((kStages - 1) * kStage + kTile + 16 * 2 * D < 65536, "stage offsets must fit the ds_read immediate");
+  auto rd_row = [&](unsigned off, int ks) -> bf16x8_t {
+    return *(const LDS_AS bf16x8_t*)(uintptr_t)(rofs[ks] + off);
+  };
+  auto rd_tr = [&](unsigned off, int db) -> bf16x8_t {
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(tofs[db][0] + off));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(uintptr_t)(tofs[db][1] + off));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4,
+                                   5, 6, 7);
+  };
+  // The hand-over buffer of a pair: lane l's 16 values as four 16-byte chunks, chunk
+  // j at (j * 64 + l) * 16, so each 16-byte access of a wave covers 1 KB in order.
+  const unsigned xbase = (unsigned)(uintptr_t)(LDS_AS char*)xch + (unsigned)(pair * kX + lane * 16);
+  auto xchg = [&](int u) -> LDS_AS f32x4_t* { return (LDS_AS f32x4_t*)(uintptr_t)(xbase + (unsigned)((u & 1) * 4 * kX)); };
+
+  // One step s of the P role: tile u = s + 1 in stage J. Loads of tile s + 3 go to
+  // the stage tile s - 1 used (last read by the dS role in step s - 1). Each phase's
+  // LDS reads are issued together ahead of the products that take them (the
+  // scheduling barriers keep the compiler from spreading them out again, one read
+  // in front of each product).
+  auto step_p = [&](auto j_tag, int s) {
+    constexpr int J = decltype(j_tag)::value;
+    constexpr unsigned CUR = J * kStage;
+    const int u = s + 1;
+    if (u < T) {
+      bf16x8_t r[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) r[ks] = rd_row(CUR, ks);
+      const LDS_AS float* l2v = (const LDS_AS float*)(uintptr_t)(lds + CUR + 2 * kTile);
+      f32x4_t l4[4];
+#pragma unroll
+      for (int part = 0; part < 4; ++part) l4[part] = *(const LDS_AS f32x4_t*)(l2v + acc_row(4 * part, g));
+      issue(s + 3, lds + (unsigned)(((J + 2) % kStages) * kStage));
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16_t sv = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sv = mfma(r[ks], kv[ks], sv);
+      bf16x8_t tr[DB][2];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        tr[db][0] = rd_tr(CUR + kTile, db);
+        tr[db][1] = rd_tr(CUR + kTile + 16 * 2 * D, db);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c, -l4[i / 4][i % 4]));
+      LDS_AS f32x4_t* x = xchg(u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[64 * j] = f32x4_t{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+      const bf16x8_t p0 = pack8(p), p1 = pack8(p + 8);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        acc[db] = mfma(tr[db][0], p0, acc[db]);
+        acc[db] = mfma(tr[db][1], p1, acc[db]);
+      }
+      // The hand-over writes must be done before the barrier that lets the partner
+      // read them, and every read of the tile before the barrier after which its
+      // stage is refilled (the barrier itself does not wait for LDS operations).
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else {
+      issue(s + 3, lds + (unsigned)(((J + 2) % kStages) * kStage));
+    }
+    // Tile s + 2 has landed (the P role reads it from the next step on); tile s + 3
+    // may stay in flight. The barrier also publishes this step's P to the partner.
+    tile_barrier<kPerTile>();
+  };
+  // One step s of the dS role: tile s in stage J.
+  auto step_ds = [&](auto j_tag, int s) {
+    constexpr int J = decltype(j_tag)::value;
+    constexpr unsigned CUR = J * kStage;
+    bf16x8_t r[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) r[ks] = rd_row(CUR + kTile, ks);
+    const LDS_AS float* dvv = (const LDS_AS float*)(uintptr_t)(lds + CUR + 2 * kTile + 256);
+    const LDS_AS f32x4_t* x = xchg(s);
+    f32x4_t d4[4], p4[4];
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      d4[part] = *(const LDS_AS f32x4_t*)(dvv + acc_row(4 * part, g));
+      p4[part] = x[64 * part];
+    }
+    issue(s + 3, lds + (unsigned)(((J + 3) % kStages) * kStage));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16_t dp = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) dp = mfma(r[ks], kv[ks], dp);
+    bf16x8_t tr[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      tr[db][0] = rd_tr(CUR, db);
+      tr[db][1] = rd_tr(CUR + 16 * 2 * D, db);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ds[i] = p4[i / 4][i % 4] * (dp[i] - d4[i / 4][i % 4]);
+    const bf16x8_t s0 = pack8(ds), s1 = pack8(ds + 8);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = mfma(tr[db][0], s0, acc[db]);
+      acc[db] = mfma(tr[db][1], s1, acc[db]);
+    }
+    // Every read of this tile must be done before the barrier after which its stage
+    // is refilled (the products that take the read values may still follow it).
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    tile_barrier<kPerTile>();  // as in step_p
+  };
+  static_assert(kStages == 4, "the unrolled loops below cover a ring of four stages");
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  issue(0, lds);
+  issue(1, lds + (unsigned)kStage);
+  tile_barrier<kPerTile>();  // tile 0 landed; tile 1 may stay in flight
+  // Step -1: the P role takes tile 0; the dS role only loads and waits.
+  if (role_p) {
+    step_p(I0{}, -1);
+    int s = 0;
+    for (; s + kStages <= T; s += kStages) {
+      step_p(I1{}, s);
+      step_p(I2{}, s + 1);
+      step_p(I3{}, s + 2);
+      step_p(I0{}, s + 3);
+    }
+    if (s < T) step_p(I1{}, s);
+    if (s + 1 < T) step_p(I2{}, s + 1);
+    if (s + 2 < T) step_p(I3{}, s + 2);
+  } else {
+    issue(2, lds + (unsigned)(2 * kStage));
+    tile_barrier<kPerTile>();
+    int s = 0;
+    for (; s + kStages <= T; s += kStages) {
+      step_ds(I0{}, s);
+      step_ds(I1{}, s + 1);
+      step_ds(I2{}, s + 2);
+      step_ds(I3{}, s + 3);
+    }
+    if (s < T) step_ds(I0{}, s);
+    if (s + 1 < T) step_ds(I1{}, s + 1);
+    if (s + 2 < T) step_ds(I2{}, s + 2);
+  }
+  // Loads issued past the last tile (zero fills) must land before the workgroup's
+  // LDS can be handed to another workgroup.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (krow < N) {
+    __bf16* out = (role_p ? dv : dk) + head + (size_t)krow * D;
+    const float f = role_p ? 1.0f : scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int col = db * 32 + 8 * i4 + 4 * g;
+        const f32x2_t a = {acc[db][4 * i4] * f, acc[db][4 * i4 + 1] * f};
+        const f32x2_t b = {acc[db][4 * i4 + 2] * f, acc[db][4 * i4 + 3] * f};
+        *(u32x2_t*)(out + col) = u32x2_t{__builtin_bit_cast(unsigned, __builtin_convertvector(a, bf16x2_t)),
+                                         __builtin_bit_cast(unsigned, __builtin_convertvector(b, bf16x2_t))};
+      }
+    }
+  }
+}
+
 template <int D>
 void launch_bwd_d(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
                   void* dq, void* dk, void* dv, int BH, int N, float scale, float* dvec, float* lse2, hipStream_t st) {
@@ -688,9 +956,15 @@ void launch_bwd_d(const void* q, const void* k, const void* v, const void* o, co
   const float c = scale * kLog2e;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)total), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, (const __bf16*)dO, dvec, lse2, (__bf16*)dq, N, tiles, total, c, scale);
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)total), dim3(256), 0, st, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, (const __bf16*)dO, dvec, lse2, (__bf16*)dk, (__bf16*)dv, N, tiles, total, c,
-                     scale);
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL(bwd_dkdv_pair_kernel<D>, dim3((unsigned)total), dim3(512), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, dvec, lse2, (__bf16*)dk, (__bf16*)dv, N,
+                       tiles, total, c, scale);
+  } else {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)total), dim3(256), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, dvec, lse2, (__bf16*)dk, (__bf16*)dv, N,
+                       tiles, total, c, scale);
+  }
 }
 
 }  // namespace
