@@ -287,8 +287,8 @@ def summarize_parity(jsonl, command, out_md="profiles/parity_gpu.md"):
         "",
         "## Forward (fused, both query-tile heights), unfused baseline, decode",
         "",
-        "| path | case | BR | rows | max\|O_ref\| | max\|dO\| | max\|dO\| (\|O\|<2) | beyond half-ulp (\|O\|>=2) "
-        "| n > 1e-2 / elements | max\|dLSE\| | E_unf | max\|dO\| / E_unf |",
+        r"| path | case | BR | rows | max\|O_ref\| | max\|dO\| | max\|dO\| (\|O\|<2) | beyond half-ulp (\|O\|>=2) "
+        r"| n > 1e-2 / elements | max\|dLSE\| | E_unf | max\|dO\| / E_unf |",
         "|---|---|---|---|---|---|---|---|---|---|---|---|",
     ]
     for r in recs:
