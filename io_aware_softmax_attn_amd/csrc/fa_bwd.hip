@@ -237,8 +237,15 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
       df[ks] = *(const bf16x8_t*)(dO + head + (size_t)qrow * D + ks * 16 + g * 8);
     }
   }
-  const float lq = qrow < N ? lse2[(size_t)bh * N + qrow] : __builtin_inff();  // padded rows: P = 0
-  const float dd = qrow < N ? dvec[(size_t)bh * N + qrow] : 0.0f;
+  float lq = qrow < N ? lse2[(size_t)bh * N + qrow] : __builtin_inff();  // padded rows: P = 0
+  float dd = qrow < N ? dvec[(size_t)bh * N + qrow] : 0.0f;
+  // Consumed here, so the compiler waits for these loads once, in the prologue. Left
+  // to the loop, it would wait for them there with vmcnt(0) every step, which also
+  // waits for the K/V tile loads in flight (it does not count the asm loads), and
+  // the tiles would no longer load ahead.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]), "+v"(df[ks]));
+  asm volatile("" : "+v"(lq), "+v"(dd));
   f32x16_t acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
