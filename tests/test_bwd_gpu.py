@@ -142,3 +142,24 @@ def test_bwd_deterministic(fa):
     g2 = run_bwd(fa, q, k, v, dO, 0.088)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+def test_bwd_concurrent_side_streams(fa):
+    """Two backward calls (d = 128 and d = 64, so both dK/dV kernels) enqueued on two
+    side streams at once give the same bits as the same calls run one after the other
+    on the current stream."""
+    announce("bwd on two side streams")
+    cases = [make_case(1, 4, 1000, 128, seed=13), make_case(2, 2, 777, 64, seed=14)]
+    want = [run_bwd(fa, q, k, v, dO, None) for (q, k, v, dO) in cases]
+    gpu = [to_gpu(*c) for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = []
+    for s, (q, k, v, dO) in zip(streams, gpu):
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            o, lse = fa.forward(q, k, v, stream=s)
+            got.append(fa.backward(q, k, v, o, lse, dO, stream=s))
+    torch.cuda.synchronize()
+    for w, g in zip(want, got):
+        for a, b in zip(w, g):
+            assert torch.equal(a, b)
