@@ -886,7 +886,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the forward shards over heads with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
 

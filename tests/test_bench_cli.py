@@ -11,7 +11,7 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
-    assert r.stdout == ""  # no JSON line for a configuration this build does not run
+    assert r.stdout == ""  # no JSON line for a configuration the library does not run
 
 
 def test_summarize_trace_needs_no_gpu(tmp_path):
