@@ -464,23 +464,29 @@ __global__ void __launch_bounds__(256, 2) dec_split_mfma_kernel(const __bf16* __
     }
   };
 
-  // The next tile's rows are loaded before the current one is processed.
-  u32x4_t kc[2][KS], vc[VL], kn[2][KS], vn[VL];
-  if (wave < ntiles) load(wave, kc, vc);
-  for (int t = wave; t < ntiles; t += 4) {
-    const bool more = t + 4 < ntiles;
-    if (more) load(t + 4, kn, vn);
-    process(t, kc, vc);
-    if (more) {
+  // This wave's tiles (wave, wave + 4, ...) alternate between two register buffers:
+  // the next tile's rows are loaded into one while the other is processed, and no
+  // tile is copied from one buffer to the other (a copy would wait for the loads
+  // just issued). The first tile is waited for here, before the loop.
+  u32x4_t ka[2][KS], va[VL], kb[2][KS], vb[VL];
+  if (wave < ntiles) {
+    load(wave, ka, va);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kc[b][ks] = kn[b][ks];
-      }
-#pragma unroll
-      for (int u = 0; u < VL; ++u) vc[u] = vn[u];
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(ka[b][ks]));
     }
+#pragma unroll
+    for (int u = 0; u < VL; ++u) asm volatile("" : "+v"(va[u]));
   }
+  int t = wave;
+  for (; t + 4 < ntiles; t += 8) {
+    load(t + 4, kb, vb);
+    process(t, ka, va);
+    if (t + 8 < ntiles) load(t + 8, ka, va);
+    process(t + 4, kb, vb);
+  }
+  if (t < ntiles) process(t, ka, va);
 
   // A lane's sum covers its own keys; the query's sum adds the four lanes holding it.
   lsum = qsum4(lsum);
