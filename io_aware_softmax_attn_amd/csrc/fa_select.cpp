@@ -71,15 +71,18 @@ Blocks select_blocks(int d, int N, int B, int H) {
 
 // Split of the key range for the decode-shaped forward (few query rows, long K/V).
 // Each (b, h) is cut into S chunks of `chunk` keys, one workgroup per chunk. The
-// split kernel streams K and V, so the grid aims at one full round of resident
-// workgroups: 256 CUs times the workgroups one CU holds at once, which the kernel's
-// register use sets: the vector kernel for one query row takes 70 VGPRs (7
-// workgroups of 4 waves); the matrix-core kernel for 2 to 16 rows takes 219 VGPRs at
-// d = 128 and 118 at d = 64 (2 and 4 workgroups). A
-// second, partial round would leave most CUs idle at the end; more, shorter chunks
-// add partial results to write and merge. Chunks hold at least 256 keys and are
-// multiples of 128 keys, a whole number of the kernel's key batches for both head
-// dimensions. Depends on the shape only, not on the device.
+// split kernel streams K and V; the grid aims at kCus times a per-kernel count of
+// workgroups per CU. For the matrix-core kernel (2 to 16 rows) that count is what
+// its registers let a CU hold at d = 128 (254 VGPRs: 2 workgroups of 4 waves); at
+// d = 64 it takes 140 VGPRs (3 workgroups) and the count is 4. For the vector
+// kernel of one query row (90 VGPRs: 5 workgroups) the count is 7: a grid of more
+// workgroups than fit at once keeps more loads in flight while the first ones
+// drain, and planning for 7 measured faster than planning for 5 (6768-6799 against
+// 6431-6450 GB/s at B=16 H=32 Nk=8192 d=128, 4 against 3 chunks per head). More,
+// shorter chunks add partial
+// results to write and merge. Chunks hold at least 256 keys and are multiples of
+// 128 keys, a whole number of the kernel's key batches for both head dimensions.
+// Depends on the shape only, not on the device.
 namespace {
 int resident_per_cu(int Nq, int d) { return Nq <= 1 ? 7 : d == 64 ? 4 : 2; }
 }  // namespace
