@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16* __restrict__
 }
 
 // ---- kernel 2: dQ ----
-// Two waves per SIMD (230 VGPRs at d = 128): one wave's softmax and LDS reads
+// Two waves per SIMD (232 VGPRs at d = 128): one wave's softmax and LDS reads
 // overlap the other's products.
 template <int D>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -396,9 +396,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const __bf16* __restrict
   }
 }
 
-// ---- kernel 3: dK and dV ----
-// Two waves per SIMD at d = 64; at d = 128 the two d x 32 accumulators, K and V
-// (192 AGPRs) and about 160 VGPRs leave room for one.
+// ---- kernel 3: dK and dV, one wave per 32 keys (run at d = 64) ----
+// Two waves per SIMD at d = 64. At d = 128 the two d x 32 accumulators, K and V
+// (192 AGPRs) and about 160 VGPRs would leave room for one, so d = 128 runs the
+// two-wave kernel below instead.
 template <int D>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                        const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
