@@ -653,6 +653,7 @@ def backward_bench(args):
     avg_ms = sum(per_ms) / len(per_ms)
     flops = 2.5 * w.flops
     tf = flops / (avg_ms * 1e-3) / 1e12
+    traffic = load_traffic(w.name, "fa_bwd", BWD_SRC)
     line = {
         "metric": metric_for(BWD_METRIC, f"B={w.B} H={w.H} N={w.N} d={w.d}"),
         "value": round(tf, 2),
@@ -674,11 +675,15 @@ def backward_bench(args):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "kernel_ms_avg": round(avg_ms, 4),
             **timing_stats(per_ms, use_graph, args.steps),
             "flops_per_launch": flops,
             "executed_flops_per_launch": 3.5 * w.flops,
+            # read q, k, v, o, dO and lse once, write dq, dk and dv once
+            "min_hbm_bytes_per_launch": w.B * w.H * w.N * (16 * w.d + 4),
+            "hbm_gb_per_s": None if traffic is None else round(traffic / (avg_ms * 1e-3) / 1e9, 1),
+            "hbm_frac_of_peak": None if traffic is None else round(traffic / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
     }
     if not args.launches_only and not args.no_cpu_baseline:

@@ -67,3 +67,51 @@ def test_metric_names_the_shape_it_measures():
     assert bench.metric_for(bench.BWD_METRIC, "B=1 H=32 N=8192 d=128") == bench.BWD_METRIC
     assert bench.metric_for(bench.DECODE_METRIC, "B=16 H=32 Nq=1 Nk=8192 d=128") == bench.DECODE_METRIC
     assert bench.metric_for(bench.METRIC, "B=4 H=16 N=1024 d=64").endswith(", B=4 H=16 N=1024 d=64")
+
+
+def _committed_traffic():
+    """(stem, workload, record) of every committed counter summary."""
+    import glob
+    import json
+
+    out = []
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json"))):
+        base = os.path.basename(path)[: -len("_traffic.json")]
+        stem = "_".join(base.split("_")[:2])  # fa_fwd, fa_bwd, fa_decode, fa_unfused
+        with open(path) as f:
+            out.append((stem, base[len(stem) + 1:], json.load(f)))
+    return out
+
+
+def test_traffic_is_read_only_while_the_kernel_source_is_unchanged(tmp_path):
+    """The bench line's HBM bytes come from a committed counter summary only while
+    the hash recorded there matches the kernel source it was measured on; an edited
+    source (here a copy with one byte appended) or a missing summary gives null."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    srcs = {"fa_fwd": bench.KERNEL_SRC, "fa_bwd": bench.BWD_SRC, "fa_decode": bench.DECODE_SRC,
+            "fa_unfused": bench.UNFUSED_SRC}
+    recs = _committed_traffic()
+    assert {stem for stem, _, _ in recs} >= {"fa_fwd", "fa_bwd", "fa_decode"}
+    for stem, workload, rec in recs:
+        src = srcs[stem]
+        assert rec["workload"] == workload
+        current = rec["kernel_source_sha256_16"] == bench.kernel_source_hash(src)
+        got = bench.load_traffic(workload, stem, src)
+        assert got == (rec["hbm_bytes_per_launch"] if current else None), (stem, workload)
+        edited = tmp_path / os.path.basename(src)
+        edited.write_bytes(open(src, "rb").read() + b"\n")
+        assert bench.load_traffic(workload, stem, str(edited)) is None, (stem, workload)
+    assert bench.load_traffic("no_such_workload", "fa_fwd") is None
+
+
+def test_traffic_records_are_self_consistent():
+    """Each summary's total is its fetch plus write bytes, and its ratio is that
+    total over the read-once minimum it records."""
+    for stem, workload, rec in _committed_traffic():
+        assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"] \
+            or abs(rec["hbm_bytes_per_launch"] - rec["fetch_bytes_per_launch"] - rec["write_bytes_per_launch"]) <= 1
+        ratio = rec["hbm_bytes_per_launch"] / rec["min_hbm_bytes_per_launch"]
+        assert abs(ratio - rec["ratio_to_min"]) <= 1e-3 * ratio, (stem, workload)
+        assert len(rec["commands"]) == 2 and "FETCH_SIZE" in rec["commands"][0] and "WRITE_SIZE" in rec["commands"][1]
