@@ -66,6 +66,12 @@ def test_select_blocks(fa):
     assert fa.fa_select_blocks(128, 8192, 1, 32)[0] == 256
     # One head of 8192 rows makes 32 tiles of 256 rows for 256 CUs: take 128 rows.
     assert fa.fa_select_blocks(128, 8192, 1, 1)[0] == 128
+    # The choices the graph-timed recheck of the model confirmed, (d, N, B, H) -> rows.
+    measured = {(128, 8192, 1, 32): 256, (128, 4096, 2, 16): 256, (128, 30001, 1, 8): 256, (128, 2048, 1, 32): 256,
+                (128, 8192, 1, 4): 128, (128, 16384, 1, 1): 128, (64, 256, 1, 1): 128, (64, 1024, 4, 16): 128,
+                (64, 2048, 4, 16): 128, (64, 2048, 2, 8): 128}
+    for (d, N, B, H), br in measured.items():
+        assert fa.fa_select_blocks(d, N, B, H)[0] == br, (d, N, B, H)
     with pytest.raises(ValueError):
         fa.fa_select_blocks(96, 128)
     with pytest.raises(ValueError):
